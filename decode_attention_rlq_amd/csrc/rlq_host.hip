@@ -1,0 +1,200 @@
+// C ABI of librlq: argument validation, split planning and kernel launches.
+// Declarations and the meaning of every argument: include/rlq.h.
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rlq_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return RLQ_OK;
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s", hipGetErrorName(e),
+           hipGetErrorString(e));
+  return RLQ_EHIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Device architecture check, cached per device ordinal.
+int check_device() {
+  static int known[64];  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= 64) return RLQ_EUNSUPPORTED;
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e);
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return known[dev] == 1 ? RLQ_OK : RLQ_EUNSUPPORTED;
+}
+
+int check_cache(const rlq_cache *c, int32_t batch) {
+  if (c == nullptr || c->codes == nullptr || c->meta == nullptr || c->rope == nullptr)
+    return RLQ_EINVAL;
+  if (!aligned(c->codes, 16) || !aligned(c->meta, 16) || !aligned(c->rope, 16)) return RLQ_EINVAL;
+  if (c->page_size != RLQ_PAGE || c->num_pages < 1) return RLQ_EINVAL;
+  if (c->sink != nullptr) {
+    if (c->n_sink < 1 || c->max_batch < batch || !aligned(c->sink, 16)) return RLQ_EINVAL;
+  }
+  if (c->recent != nullptr) {
+    if (c->n_recent < 1 || c->max_batch < batch || !aligned(c->recent, 16)) return RLQ_EINVAL;
+  }
+  if (c->n_sink < 0 || c->n_recent < 0) return RLQ_EINVAL;
+  return RLQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rlq_abi_version(void) { return RLQ_ABI_VERSION; }
+
+rlq_layer_params rlq_layer_params_default(void) {
+  rlq_layer_params p;
+  p.tau = 0.9816f;
+  p.gain = 1.0f;
+  p.level_inner = 0.4528f;
+  p.level_outer = 1.510f;
+  return p;
+}
+
+const char *rlq_status_string(int status) {
+  switch (status) {
+    case RLQ_OK: return "RLQ_OK";
+    case RLQ_EINVAL: return "RLQ_EINVAL: invalid argument";
+    case RLQ_EUNSUPPORTED: return "RLQ_EUNSUPPORTED: device is not gfx950";
+    case RLQ_ENOSPC: return "RLQ_ENOSPC: workspace too small";
+    case RLQ_EHIP: return "RLQ_EHIP: HIP runtime error";
+    default: return "unknown rlq status";
+  }
+}
+
+const char *rlq_last_hip_error(void) { return g_last_hip_error; }
+
+float rlq_coupled_gain(float tau, float level_inner, float level_outer) {
+  if (!(level_inner > 0.f) || !(level_outer > 0.f)) return NAN;
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  const double t = tau;
+  const double phi0 = inv_sqrt_2pi;
+  const double phit = inv_sqrt_2pi * exp(-0.5 * t * t);
+  const double resp = 2.0 * (level_inner * phi0 + ((double)level_outer - level_inner) * phit);
+  return (float)(1.0 / resp);
+}
+
+int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
+                        const uint16_t *latent_bf16, const float *latent_rot_f32,
+                        const uint16_t *rotation_bf16, const uint16_t *k_rope_bf16,
+                        const int32_t *cu_seqlens, const int32_t *start_pos,
+                        const int32_t *block_table, int32_t max_pages_per_req,
+                        int32_t batch, int64_t n_tokens, float *z_debug, void *stream) {
+  if (p == nullptr || batch < 1 || n_tokens < 0 || max_pages_per_req < 1) return RLQ_EINVAL;
+  int st = check_cache(cache, batch);
+  if (st != RLQ_OK) return st;
+  if ((latent_bf16 == nullptr) == (latent_rot_f32 == nullptr)) return RLQ_EINVAL;
+  if (latent_bf16 != nullptr && (rotation_bf16 == nullptr || !aligned(latent_bf16, 16) ||
+                                 !aligned(rotation_bf16, 16)))
+    return RLQ_EINVAL;
+  if (latent_rot_f32 != nullptr && !aligned(latent_rot_f32, 16)) return RLQ_EINVAL;
+  if (k_rope_bf16 == nullptr || !aligned(k_rope_bf16, 16)) return RLQ_EINVAL;
+  if (cu_seqlens == nullptr || start_pos == nullptr || block_table == nullptr) return RLQ_EINVAL;
+  if (!aligned(cu_seqlens, 4) || !aligned(start_pos, 4) || !aligned(block_table, 4)) return RLQ_EINVAL;
+  if (z_debug != nullptr && !aligned(z_debug, 16)) return RLQ_EINVAL;
+  st = check_device();
+  if (st != RLQ_OK) return st;
+  if (n_tokens == 0) return RLQ_OK;
+
+  rlq::AppendArgs a;
+  a.latent = latent_bf16;
+  a.latent_rot = latent_rot_f32;
+  a.rotation = rotation_bf16;
+  a.k_rope = k_rope_bf16;
+  a.cu_seqlens = cu_seqlens;
+  a.start_pos = start_pos;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_req;
+  a.batch = batch;
+  a.n_tokens = n_tokens;
+  a.codes = cache->codes;
+  a.meta = cache->meta;
+  a.rope = cache->rope;
+  a.sink = cache->sink;
+  a.recent = cache->recent;
+  a.n_sink = cache->sink ? cache->n_sink : 0;
+  a.n_recent = cache->recent ? cache->n_recent : 0;
+  a.tau = p->tau;
+  a.z_debug = z_debug;
+  return hip_status(rlq::launch_append(a, (hipStream_t)stream));
+}
+
+int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
+                                  size_t *bytes) {
+  if (bytes == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16 ||
+      max_ctx_len < 0)
+    return RLQ_EINVAL;
+  *bytes = rlq::decode_workspace_bytes(batch, heads, rlq::plan_splits(batch, heads, max_ctx_len));
+  return RLQ_OK;
+}
+
+int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
+                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                   int32_t batch, int32_t heads, float sm_scale,
+                   const int32_t *block_table, int32_t max_pages_per_req,
+                   const int32_t *ctx_lens, int32_t max_ctx_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  if (p == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16)
+    return RLQ_EINVAL;
+  if (max_ctx_len < 0 || max_pages_per_req < 1 ||
+      (int64_t)max_ctx_len > (int64_t)max_pages_per_req * RLQ_PAGE)
+    return RLQ_EINVAL;
+  int st = check_cache(cache, batch);
+  if (st != RLQ_OK) return st;
+  if (q_c_bf16 == nullptr || q_r_bf16 == nullptr || block_table == nullptr ||
+      ctx_lens == nullptr || out == nullptr || workspace == nullptr)
+    return RLQ_EINVAL;
+  if (!aligned(q_c_bf16, 16) || !aligned(q_r_bf16, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return RLQ_EINVAL;
+  const rlq::SplitPlan plan = rlq::plan_splits(batch, heads, max_ctx_len);
+  if (workspace_bytes < rlq::decode_workspace_bytes(batch, heads, plan)) return RLQ_ENOSPC;
+  st = check_device();
+  if (st != RLQ_OK) return st;
+
+  rlq::DecodeArgs a;
+  a.codes = cache->codes;
+  a.meta = cache->meta;
+  a.rope = cache->rope;
+  a.sink = cache->sink;
+  a.recent = cache->recent;
+  a.n_sink = cache->sink ? cache->n_sink : 0;
+  a.n_recent = cache->recent ? cache->n_recent : 0;
+  a.q_c = q_c_bf16;
+  a.q_r = q_r_bf16;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_req;
+  a.ctx_lens = ctx_lens;
+  a.heads = heads;
+  a.tokens_per_split = plan.tokens_per_split;
+  a.splits = plan.splits;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.gain = p->gain;
+  a.level_inner = p->level_inner;
+  a.level_outer = p->level_outer;
+  const size_t parts = (size_t)batch * (heads / 16) * plan.splits;
+  a.part_o = (float *)workspace;
+  a.part_ml = a.part_o + parts * rlq::kPartialFloats;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(rlq::launch_decode(a, batch, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal declarations shared by the librlq translation units (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlq.h"
+
+namespace rlq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- append
+
+struct AppendArgs {
+  const uint16_t *latent;      // [N][512] bf16, or null
+  const float *latent_rot;     // [N][512] fp32, or null
+  const uint16_t *rotation;    // [512][512] bf16
+  const uint16_t *k_rope;      // [N][64] bf16
+  const int32_t *cu_seqlens;   // [B+1]
+  const int32_t *start_pos;    // [B]
+  const int32_t *block_table;  // [B][max_pages]
+  int32_t max_pages;
+  int32_t batch;
+  int64_t n_tokens;
+  uint32_t *codes;
+  float *meta;
+  uint16_t *rope;
+  uint16_t *sink;
+  uint16_t *recent;
+  int32_t n_sink;
+  int32_t n_recent;
+  float tau;
+  float *z_debug;
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+
+// Tokens of one wave iteration and of one score tile.
+constexpr int kChunk = 32;
+constexpr int kTile = 16;
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// Per-(request, head group, split) partial: 16 heads x 512 latent fp32 in the
+// accumulator's own order, then (max, sum) per head.
+constexpr int kPartialFloats = 16 * RLQ_DC;
+
+struct DecodeArgs {
+  const uint32_t *codes;
+  const float *meta;
+  const uint16_t *rope;
+  const uint16_t *sink;
+  const uint16_t *recent;
+  int32_t n_sink;
+  int32_t n_recent;
+  const uint16_t *q_c;
+  const uint16_t *q_r;
+  const int32_t *block_table;
+  int32_t max_pages;
+  const int32_t *ctx_lens;
+  int32_t heads;
+  int32_t tokens_per_split;
+  int32_t splits;
+  float scale_log2;  // sm_scale * log2(e)
+  float gain;
+  float level_inner;
+  float level_outer;
+  float *part_o;   // [B][HG][S][kPartialFloats]
+  float *part_ml;  // [B][HG][S][16][2]
+  float *out;      // [B][H][512]
+  float *lse;      // [B][H] or null
+};
+
+// Split policy shared by the workspace query and the launch.
+struct SplitPlan {
+  int32_t tokens_per_split;
+  int32_t splits;
+};
+SplitPlan plan_splits(int32_t batch, int32_t heads, int32_t max_ctx_len);
+size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &plan);
+
+hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream);
+
+}  // namespace rlq

@@ -1,0 +1,230 @@
+/*
+ * rlq.h - C ABI of librlq: RoLaQ-style 2-bit MLA latent cache on MI355X (gfx950).
+ *
+ * The library implements the data-parallel hot path of a 2-bit Multi-Head
+ * Latent Attention cache as described in "RoLaQ: Joint Rotation and Range
+ * Calibration for 2-Bit KV Caches in Multi-Head Latent Attention":
+ *
+ *   rlq_quantize_append  write side: rotate each token's content latent by the
+ *                        fixed shared rotation (§3.3), standardize every
+ *                        128-coordinate group with an fp32 mean and scale
+ *                        (§A.3), assign each coordinate one of four levels by
+ *                        the per-layer threshold tau (§3.2), pack the 2-bit
+ *                        codes and copy the BF16 RoPE key (§2.1, §A.3);
+ *                        optionally keep sink/recent tokens in BF16 (§4.1).
+ *   rlq_mla_decode       read side: absorbed-MLA decode attention over the
+ *                        paged cache; reconstruction = group mean + scale *
+ *                        gain * level (§3.2); scores q_c.c_hat + q_R.k_R with
+ *                        the read-side rotation folded into the absorbed query
+ *                        (§3.3, Fig. 3a); softmax; output in latent space.
+ *
+ * Storage per unprotected token and layer: 128 B codes + 32 B fp32 group
+ * statistics + 128 B BF16 RoPE key = 288 B (§A.3; the storage-accounting
+ * notebook "What does a 2-bit KV cache actually store?").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers marked "device" are HIP device pointers; the caller allocates
+ *    and owns them.  The library allocates nothing, keeps no pointer after a
+ *    call returns, holds no global state, and never synchronizes: work is
+ *    enqueued on `stream` and the caller keeps every buffer alive until the
+ *    stream has completed it.
+ *  - Device pointers must be 16-byte aligned and their arrays contiguous in
+ *    the layouts given below.
+ *  - Each call returns an RLQ_* status.  Host-side validation runs before any
+ *    launch; on error nothing is enqueued.  A launch failure reported by the
+ *    HIP runtime returns RLQ_EHIP (text via rlq_last_hip_error()).
+ *  - Values that live in device memory (block tables, lengths, positions) are
+ *    trusted: out-of-range entries are undefined behaviour.
+ *  - Calls on one stream run in order; calls that overlap on different
+ *    streams must not write the same cache slots.
+ *  - Values: content latents must stay within the fp16 range (|x| < 65504);
+ *    non-finite inputs are outside the method's domain.
+ */
+#ifndef RLQ_H
+#define RLQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLQ_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  RLQ_OK = 0,
+  RLQ_EINVAL = -1,        /* bad argument: null/misaligned pointer, bad size      */
+  RLQ_EUNSUPPORTED = -2,  /* current device is not gfx950                          */
+  RLQ_ENOSPC = -3,        /* workspace too small                                   */
+  RLQ_EHIP = -4           /* HIP runtime error while launching                     */
+};
+
+/* Fixed dimensions (DeepSeek-V2-Lite MLA: latent 512, RoPE 64; group 128). */
+#define RLQ_DC 512        /* content latent width d_c                              */
+#define RLQ_DR 64         /* RoPE key width d_R                                    */
+#define RLQ_GROUP 128     /* coordinates per (mean, scale) group                   */
+#define RLQ_NGROUPS 4     /* groups per token                                      */
+#define RLQ_PAGE 64       /* tokens per cache page                                 */
+#define RLQ_WORDS 32      /* uint32 code words per token (16 codes per word)       */
+#define RLQ_MAX_HEADS 128
+
+/*
+ * Per-layer quantizer parameters, fixed while serving (§3.3).
+ *   tau          threshold on the standardized coordinate (§3.2, §C.3)
+ *   gain         reconstruction gain around the group mean (§3.2, §B.3)
+ *   level_inner  a, level_outer b: the four levels are -b, -a, +a, +b
+ * Defaults (rlq_layer_params_default): the four-level Lloyd-Max quantizer for
+ * a unit Gaussian, tau 0.9816, levels 0.4528 / 1.510, gain 1 (the initial
+ * threshold named in §C.3 and Fig. 8).
+ */
+typedef struct {
+  float tau;
+  float gain;
+  float level_inner;
+  float level_outer;
+} rlq_layer_params;
+
+/*
+ * Paged cache of one layer (device memory, caller-owned).
+ *   codes   uint32 [num_pages][64][32]  2-bit codes, 16 per word; coordinate
+ *                                       j of a token is word j/16, bits
+ *                                       2*(j%16) .. 2*(j%16)+1; code 0,1,2,3 =
+ *                                       level -b, -a, +a, +b
+ *   meta    float  [num_pages][64][8]   mu_0..mu_3, s_0..s_3 per token
+ *   rope    uint16 [num_pages][64][64]  BF16 RoPE key per token
+ *   sink    uint16 [max_batch][n_sink][512]   BF16 rotated latent of positions
+ *                                       0..n_sink-1 of each request, or NULL
+ *   recent  uint16 [max_batch][n_recent][512] BF16 rotated latent ring; the
+ *                                       token at position p sits in slot
+ *                                       p % n_recent; or NULL
+ *   page_size must be 64.  Protection (§4.1, §A.3): with sink/recent given,
+ *   decode reads those tokens' content from them instead of the codes.
+ */
+typedef struct {
+  uint32_t *codes;
+  float *meta;
+  uint16_t *rope;
+  int32_t num_pages;
+  int32_t page_size;
+  uint16_t *sink;
+  uint16_t *recent;
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t max_batch;
+} rlq_cache;
+
+/* Library ABI version (RLQ_ABI_VERSION). */
+int rlq_abi_version(void);
+
+/* Default quantizer parameters (see rlq_layer_params). */
+rlq_layer_params rlq_layer_params_default(void);
+
+/* Static text for a status code. */
+const char *rlq_status_string(int status);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char *rlq_last_hip_error(void);
+
+/*
+ * Gain linked to tau for unit response of the centred signal (§3.2, §B.3),
+ * for x ~ N(0,1):  g(tau) = 1 / (2 (a phi(0) + (b - a) phi(tau))).
+ * Host-only helper; returns NaN for non-positive levels.
+ */
+float rlq_coupled_gain(float tau, float level_inner, float level_outer);
+
+/*
+ * rlq_quantize_append - append new tokens of `batch` requests to the cache.
+ *
+ * Request b owns new tokens cu_seqlens[b] .. cu_seqlens[b+1]-1; its i-th new
+ * token lands at position p = start_pos[b] + i, in page block_table[b][p / 64]
+ * slot p % 64.  For every token:
+ *   z     = R c (fp32), or the given already-rotated latent;
+ *   mu_g  = S(z_g) / 128, d = z - mu_g, s_g = sqrt(S(d*d) / 128), where S is
+ *           the fp32 adjacent-pair tree sum over the group, d*d is a plain
+ *           fp32 product and sqrt is correctly rounded;
+ *   code  = [d >= -t] + [d >= 0] + [d >= t] with t = fl32(tau * s_g);
+ * and codes, meta, rope are written.  With cache->sink, positions p < n_sink
+ * also write sink[b][p] = bf16(z); with cache->recent, the last n_recent
+ * positions of the request after this append write recent[b][p % n_recent].
+ *
+ *   p              layer parameters (host pointer; tau used here)
+ *   cache          cache descriptor (host pointer to device pools)
+ *   latent_bf16    device [n_tokens][512] BF16 content latents, or NULL
+ *   latent_rot_f32 device [n_tokens][512] fp32 rotated latents z, or NULL;
+ *                  exactly one of latent_bf16 / latent_rot_f32 is non-NULL
+ *   rotation_bf16  device [512][512] BF16 rotation R (row = output),
+ *                  required with latent_bf16, ignored otherwise
+ *   k_rope_bf16    device [n_tokens][64] BF16 RoPE keys
+ *   cu_seqlens     device int32 [batch+1], cu_seqlens[0] = 0, non-decreasing
+ *   start_pos      device int32 [batch], tokens already cached per request
+ *   block_table    device int32 [batch][max_pages_per_req] page ids
+ *   batch          number of requests, 1 .. max_batch when protection is on
+ *   n_tokens       host copy of cu_seqlens[batch] (sizes the launch; 0 = no-op)
+ *   z_debug        device [n_tokens][512] fp32 dump of z, or NULL
+ *
+ * With latent_bf16 the rotation runs as a bf16 MFMA product with fp32
+ * accumulation; with identity or signed-permutation R every z is exact.
+ * Errors: RLQ_EINVAL (null/misaligned pointers, page_size != 64, batch < 1,
+ * n_tokens < 0, both or neither latent given, protection buffers without
+ * max_batch >= batch), RLQ_EUNSUPPORTED, RLQ_EHIP.
+ */
+int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
+                        const uint16_t *latent_bf16, const float *latent_rot_f32,
+                        const uint16_t *rotation_bf16, const uint16_t *k_rope_bf16,
+                        const int32_t *cu_seqlens, const int32_t *start_pos,
+                        const int32_t *block_table, int32_t max_pages_per_req,
+                        int32_t batch, int64_t n_tokens, float *z_debug,
+                        void *stream);
+
+/*
+ * Workspace (bytes) that rlq_mla_decode needs for this batch, head count and
+ * maximum context length: split-KV partials (unnormalised output, running max
+ * and sum per split and head).  Errors: RLQ_EINVAL.
+ */
+int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
+                                  size_t *bytes);
+
+/*
+ * rlq_mla_decode - one decode step of absorbed MLA attention over the cache.
+ *
+ * For request b and head h, over positions t < ctx_lens[b]:
+ *   c_hat_t = mu + s * gain * L[code]    (or the BF16 sink/recent latent)
+ *   s_t     = sm_scale * (q_c[b,h] . c_hat_t + q_r[b,h] . k_R_t)
+ *   out     = sum_t softmax(s)_t c_hat_t,   lse = ln sum_t exp(s_t)
+ * Tokens t < n_sink read sink[b][t]; tokens t >= ctx_len - n_recent read
+ * recent[b][t % n_recent] (when those buffers are given); the RoPE key always
+ * comes from rope.  With protection the ring must hold the request's last
+ * n_recent tokens, i.e. ctx_lens[b] equals the cached length.
+ *
+ *   q_c_bf16       device [batch][heads][512] absorbed content queries (BF16),
+ *                  already in the rotated basis
+ *   q_r_bf16       device [batch][heads][64] RoPE queries (BF16)
+ *   heads          multiple of 16, at most 128
+ *   sm_scale       softmax scale
+ *   block_table    device int32 [batch][max_pages_per_req]
+ *   ctx_lens       device int32 [batch], 0 <= ctx_lens[b] <= max_ctx_len
+ *   max_ctx_len    host bound on ctx_lens (sizes the split grid)
+ *   out            device fp32 [batch][heads][512]
+ *   lse            device fp32 [batch][heads] natural-log LSE, or NULL
+ *   workspace      device scratch of at least rlq_mla_decode_workspace_size()
+ *                  bytes; its contents need no initialisation
+ * ctx_lens[b] = 0 gives out = 0 and lse = -inf.
+ * Errors: RLQ_EINVAL (pointers, heads, batch, max_ctx_len beyond the block
+ * table), RLQ_ENOSPC, RLQ_EUNSUPPORTED, RLQ_EHIP.
+ */
+int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
+                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                   int32_t batch, int32_t heads, float sm_scale,
+                   const int32_t *block_table, int32_t max_pages_per_req,
+                   const int32_t *ctx_lens, int32_t max_ctx_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLQ_H */

@@ -1,0 +1,109 @@
+"""Shared helpers for the GPU parity tests: move seeded inputs to the device,
+build oracle caches, compare results.  The oracle side and the HIP side only
+meet here, on the same seeded inputs."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_rlq_amd import rlq
+
+OUT_TOL = 2e-3   # row-normalised max relative error of the decode output
+LSE_TOL = 2e-3   # absolute error of the natural-log LSE
+
+
+def dev(x: np.ndarray, dtype=None) -> torch.Tensor:
+    """numpy -> cuda tensor; uint16 arrays are bf16 bit patterns, uint32 are code words."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    if x.dtype == np.uint32:
+        return torch.from_numpy(x.view(np.int32)).cuda()
+    t = torch.from_numpy(x)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """cuda tensor -> numpy with the bit patterns of include/rlq.h."""
+    a = t.detach().cpu()
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    if a.dtype == torch.int32:
+        return a.numpy().view(np.uint32)
+    return a.numpy()
+
+
+def params_of(prob) -> rlq.LayerParams:
+    return rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+
+
+def oracle_cache_for(prob, *, z=None, protect=True):
+    """Cache written by the oracle from the problem's latents (or a given z)."""
+    cache = oracle.new_cache(prob.num_pages, max_batch=prob.batch,
+                             n_sink=prob.n_sink if protect else 0,
+                             n_recent=prob.n_recent if protect else 0)
+    kw = dict(latent_rot_f32=z) if z is not None else dict(
+        latent_bf16=prob.latent_bits, rotation_bf16=prob.rotation_bits)
+    zz = oracle.quantize_append(cache, prob.tau, prob.k_rope_bits, prob.cu_seqlens,
+                                prob.start_pos, prob.block_table, **kw)
+    return cache, zz
+
+
+def device_cache_from(cache: oracle.Cache) -> rlq.PagedCache:
+    return rlq.PagedCache(codes=dev(cache.codes), meta=dev(cache.meta), rope=dev(cache.rope),
+                          sink=None if cache.sink is None else dev(cache.sink),
+                          recent=None if cache.recent is None else dev(cache.recent))
+
+
+def empty_device_cache(prob, protect=True, fill=None) -> rlq.PagedCache:
+    c = rlq.PagedCache.allocate(prob.num_pages, max_batch=prob.batch,
+                                n_sink=prob.n_sink if protect else 0,
+                                n_recent=prob.n_recent if protect else 0)
+    if fill is not None:
+        for t in (c.codes, c.meta, c.rope, c.sink, c.recent):
+            if t is not None:
+                t.view(torch.int16 if t.element_size() == 2 else torch.int32).fill_(fill)
+    return c
+
+
+def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """max over (request, head) of max_j |out - ref| / max_j |ref|."""
+    num = np.abs(out - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+def check_decode(out, lse, ref_out, ref_lse, ctx_lens):
+    out = out.detach().cpu().numpy().astype(np.float64)
+    lse = lse.detach().cpu().numpy().astype(np.float64)
+    ctx = np.asarray(ctx_lens)
+    empty = ctx == 0
+    if empty.any():
+        assert np.all(out[empty] == 0)
+        assert np.all(np.isneginf(lse[empty]))
+    full = ~empty
+    err = row_rel_err(out[full], ref_out[full]) if full.any() else 0.0
+    lerr = float(np.abs(lse[full] - ref_lse[full]).max()) if full.any() else 0.0
+    assert np.isfinite(out).all()
+    assert err <= OUT_TOL, f"output row-relative error {err:.3e} > {OUT_TOL}"
+    assert lerr <= LSE_TOL, f"lse error {lerr:.3e} > {LSE_TOL}"
+    return err, lerr
+
+
+def run_decode(prob, cache: rlq.PagedCache, max_ctx_len=None, ctx_lens=None):
+    ctx = prob.ctx_lens if ctx_lens is None else np.asarray(ctx_lens, np.int32)
+    mcl = int(ctx.max()) if max_ctx_len is None else max_ctx_len
+    out, lse = rlq.mla_decode(params_of(prob), cache, dev(prob.q_c_bits), dev(prob.q_r_bits),
+                              prob.sm_scale, dev(prob.block_table), dev(ctx.astype(np.int32)), mcl)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_decode(prob, cache: oracle.Cache, ctx_lens=None, heads=None):
+    ctx = prob.ctx_lens if ctx_lens is None else ctx_lens
+    return oracle.decode(cache, prob.q_c_bits, prob.q_r_bits, prob.sm_scale, prob.block_table,
+                         ctx, prob.gain, prob.level_inner, prob.level_outer, heads=heads)

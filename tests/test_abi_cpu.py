@@ -1,0 +1,101 @@
+"""The C-ABI library loads and exports every symbol include/rlq.h declares.
+
+CPU only: nothing here launches a kernel or touches a device.  The calls made
+are the host-only helpers and argument validation that fails before any HIP
+call.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_rlq_amd import rlq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rlq.LIB_PATH):
+        from decode_attention_rlq_amd import build
+        build.build()
+    return rlq.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(rlq.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_defaults(lib):
+    assert rlq.abi_version() == 1
+    p = rlq.default_params()
+    assert (p.tau, p.gain, p.level_inner, p.level_outer) == (
+        np.float32(0.9816), 1.0, np.float32(0.4528), np.float32(1.510))
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert lib.rlq_status_string(s).startswith(b"RLQ_")
+    assert lib.rlq_status_string(7) == b"unknown rlq status"
+
+
+def test_coupled_gain_matches_oracle(lib):
+    tau, a, b, _ = oracle.lloyd_max_gaussian()
+    for t in (0.85, 0.91, tau, 1.1):
+        g = rlq.coupled_gain(t, a, b)
+        assert abs(g - oracle.coupled_gain(t, np.float32(a), np.float32(b))) < 1e-6
+    assert np.isnan(rlq.coupled_gain(0.9, 0.0, 1.5))
+
+
+def test_workspace_size(lib):
+    n1 = rlq.decode_workspace_size(4, 16, 262144)
+    n2 = rlq.decode_workspace_size(4, 32, 262144)
+    assert n1 > 0 and n2 > 0 and n1 % 16 == 0 and n2 % 16 == 0
+    assert rlq.decode_workspace_size(1, 16, 0) > 0
+    with pytest.raises(ValueError):
+        rlq.decode_workspace_size(1, 24, 100)
+    with pytest.raises(ValueError):
+        rlq.decode_workspace_size(0, 16, 100)
+    with pytest.raises(ValueError):
+        rlq.decode_workspace_size(1, 144, 100)
+
+
+def test_validation_rejects_before_any_launch(lib):
+    p = rlq.default_params()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+    good = rlq.CacheDesc(0x100000, 0x100000, 0x100000, 4, 64, None, None, 0, 0, 0)
+    bad_page = rlq.CacheDesc(0x100000, 0x100000, 0x100000, 4, 32, None, None, 0, 0, 0)
+    misaligned = rlq.CacheDesc(0x100004, 0x100000, 0x100000, 4, 64, None, None, 0, 0, 0)
+    no_max_batch = rlq.CacheDesc(0x100000, 0x100000, 0x100000, 4, 64, 0x100000, None, 4, 0, 0)
+    A = lib.rlq_quantize_append
+    # neither latent form
+    assert A(ctypes.byref(p), ctypes.byref(good), None, None, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    # both latent forms
+    assert A(ctypes.byref(p), ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    # latent without rotation
+    assert A(ctypes.byref(p), ctypes.byref(good), fake, None, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    for c in (bad_page, misaligned, no_max_batch):
+        assert A(ctypes.byref(p), ctypes.byref(c), None, fake, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    assert A(ctypes.byref(p), ctypes.byref(good), None, fake, None, fake, fake, fake, fake, 1, 0, 8, None, None) == -1
+    assert A(None, ctypes.byref(good), None, fake, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    D = lib.rlq_mla_decode
+    args = lambda heads, mcl, ws: (ctypes.byref(p), ctypes.byref(good), fake, fake, 1, heads, 0.1,
+                                   fake, 4, fake, mcl, fake, None, fake, ws, None)
+    assert D(*args(8, 64, 1 << 30)) == -1       # heads not a multiple of 16
+    assert D(*args(256, 64, 1 << 30)) == -1     # too many heads
+    assert D(*args(16, 257, 1 << 30)) == -1     # context beyond the block table
+    assert D(*args(16, 256, 16)) == -3          # workspace too small

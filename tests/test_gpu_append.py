@@ -1,0 +1,147 @@
+"""GPU parity of rlq_quantize_append against the oracle (codes bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_rlq_amd import rlq, workloads
+from gpu_helpers import dev, empty_device_cache, host_bits, oracle_cache_for, params_of
+
+pytestmark = pytest.mark.gpu
+
+
+def appended(prob, new_lens, start_pos):
+    """Keep only positions start_pos[b] .. start_pos[b]+new_lens[b]-1 of each request as new tokens."""
+    lat, kr, cu = [], [], [0]
+    for b in range(prob.batch):
+        lo = int(prob.cu_seqlens[b]) + int(start_pos[b])
+        lat.append(prob.latent_bits[lo:lo + new_lens[b]])
+        kr.append(prob.k_rope_bits[lo:lo + new_lens[b]])
+        cu.append(cu[-1] + int(new_lens[b]))
+    prob.latent_bits = np.concatenate(lat)
+    prob.k_rope_bits = np.concatenate(kr)
+    prob.cu_seqlens = np.asarray(cu, np.int32)
+    prob.start_pos = np.asarray(start_pos, np.int32)
+    return prob
+
+
+def compare_pools(dc, oc):
+    assert np.array_equal(host_bits(dc.codes), oc.codes), "codes differ"
+    assert np.array_equal(host_bits(dc.meta).view(np.uint32), oc.meta.view(np.uint32)), "meta differ"
+    assert np.array_equal(host_bits(dc.rope), oc.rope), "rope differ"
+    if oc.sink is not None:
+        assert np.array_equal(host_bits(dc.sink), oc.sink), "sink differ"
+    if oc.recent is not None:
+        assert np.array_equal(host_bits(dc.recent), oc.recent), "recent differ"
+
+
+def gpu_append(prob, dc, *, z=None, rotation_bits=None):
+    kw = dict(latent_rot=dev(z)) if z is not None else dict(
+        latent=dev(prob.latent_bits), rotation=dev(prob.rotation_bits if rotation_bits is None else rotation_bits))
+    rlq.quantize_append(params_of(prob), dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens),
+                        dev(prob.start_pos), dev(prob.block_table), **kw)
+    torch.cuda.synchronize()
+
+
+CASES = {
+    "tiny": dict(name="tiny"),
+    "ragged_offsets": dict(name="tiny", ctx_lens=[37, 6, 130, 128, 200], start=[0, 5, 27, 64, 3],
+                           n_sink=4, n_recent=16),
+    "protect_4_64": dict(name="ragged_protect", ctx_lens=[70, 1, 300], start=[0, 0, 100],
+                         heads=16, n_sink=4, n_recent=64),
+}
+
+
+def build(case):
+    c = dict(CASES[case])
+    start = c.pop("start", None)
+    prob = workloads.make_problem(c.pop("name"), **c)
+    if start is not None:
+        new = [int(n) - int(s) for n, s in zip(prob.ctx_lens, start)]
+        prob = appended(prob, new, start)
+    return prob
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_append_prerotated_bitexact(case):
+    prob = build(case)
+    z = oracle.rotate(prob.latent_bits, prob.rotation_bits)
+    oc, _ = oracle_cache_for(prob, z=z)
+    dc = empty_device_cache(prob)
+    gpu_append(prob, dc, z=z)
+    compare_pools(dc, oc)
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged_offsets"])
+def test_append_signed_permutation_exact_end_to_end(case):
+    prob = build(case)
+    perm = workloads.signed_permutation(np.random.default_rng(5), 512)
+    prob.rotation_bits = workloads.to_bf16_bits(perm)
+    oc, _ = oracle_cache_for(prob)
+    dc = empty_device_cache(prob)
+    gpu_append(prob, dc)
+    compare_pools(dc, oc)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_append_haar_rotation(case):
+    """Haar rotation through bf16 MFMA: the encoder applied to the GPU's own z is
+    bit-exact; z is within the fp32 accumulation bound of the exact product;
+    codes that differ from the oracle's sit at a cut point within that bound."""
+    prob = build(case)
+    n = prob.n_tokens
+    dc = empty_device_cache(prob)
+    zdbg = torch.empty((n, 512), dtype=torch.float32, device="cuda")
+    rlq.quantize_append(params_of(prob), dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens),
+                        dev(prob.start_pos), dev(prob.block_table), latent=dev(prob.latent_bits),
+                        rotation=dev(prob.rotation_bits), z_debug=zdbg)
+    torch.cuda.synchronize()
+    z_gpu = zdbg.cpu().numpy()
+    oc_gpu_z, _ = oracle_cache_for(prob, z=z_gpu)
+    compare_pools(dc, oc_gpu_z)
+    # Accumulation bound: |z_gpu - z| <= gamma_512 * sum_k |R_ik c_k| (+ fp32 rounding of z).
+    c = oracle.bf16_bits_to_f64(prob.latent_bits)
+    r = oracle.bf16_bits_to_f64(prob.rotation_bits)
+    z_exact = c @ r.T
+    bound = (512 * 2.0 ** -24 / (1 - 512 * 2.0 ** -24)) * (np.abs(c) @ np.abs(r).T) + np.abs(z_exact) * 2.0 ** -24
+    assert np.all(np.abs(z_gpu - z_exact) <= bound)
+    # Codes that differ from the oracle's own encoding are boundary cases only.
+    z_or = z_exact.astype(np.float32)
+    w_o, m_o = oracle.encode_tokens(z_or, prob.tau)
+    w_g, m_g = oracle.encode_tokens(z_gpu, prob.tau)
+    co, cg = oracle.unpack_codes(w_o), oracle.unpack_codes(w_g)
+    diff = co != cg
+    frac = diff.mean()
+    assert frac < 1e-3, f"{diff.sum()} codes differ"
+    if diff.any():
+        mu, s, d = oracle.group_stats(z_or)
+        t = (np.float32(prob.tau) * s).repeat(128, axis=1)
+        dist = np.minimum(np.minimum(np.abs(d - t), np.abs(d + t)), np.abs(d))
+        slack = bound.max(axis=1, keepdims=True) * 4 + np.abs(m_o - m_g).max(axis=1, keepdims=True)
+        assert np.all(dist[diff] <= np.broadcast_to(slack, d.shape)[diff])
+
+
+def test_append_empty_is_noop():
+    prob = workloads.make_problem("tiny")
+    dc = empty_device_cache(prob, fill=0x5A5A)
+    before = host_bits(dc.codes).copy()
+    rlq.quantize_append(params_of(prob), dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens),
+                        dev(prob.start_pos), dev(prob.block_table), latent=dev(prob.latent_bits),
+                        rotation=dev(prob.rotation_bits), n_tokens=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dc.codes), before)
+
+
+def test_append_invalid_arguments_raise():
+    prob = workloads.make_problem("tiny")
+    dc = empty_device_cache(prob)
+    p = params_of(prob)
+    with pytest.raises(ValueError):  # both latent forms given
+        rlq.quantize_append(p, dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens), dev(prob.start_pos),
+                            dev(prob.block_table), latent=dev(prob.latent_bits),
+                            latent_rot=torch.zeros((256, 512), device="cuda"),
+                            rotation=dev(prob.rotation_bits))
+    with pytest.raises(ValueError):  # latent without rotation
+        rlq.quantize_append(p, dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens), dev(prob.start_pos),
+                            dev(prob.block_table), latent=dev(prob.latent_bits))

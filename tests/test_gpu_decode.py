@@ -1,0 +1,138 @@
+"""GPU parity of rlq_mla_decode against the oracle (outputs within 2e-3)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_rlq_amd import rlq, workloads
+from gpu_helpers import (check_decode, dev, device_cache_from, empty_device_cache, oracle_cache_for,
+                         oracle_decode, params_of, run_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+def z_of(prob):
+    return oracle.rotate(prob.latent_bits, prob.rotation_bits)
+
+
+DECODE_CASES = {
+    # name: make_problem keyword arguments
+    "tiny": dict(name="tiny"),
+    "tails_h16": dict(name="v2lite_32k", ctx_lens=[1, 17, 31, 32, 33, 63, 64, 65, 100, 257, 1000, 4097]),
+    "tails_h32": dict(name="v2lite_32k", ctx_lens=[5, 129, 640, 2049], heads=32),
+    "v2lite_4x8k": dict(name="v2lite_32k", ctx=8192),
+    "protect_4_64": dict(name="ragged_protect", ctx_lens=[5, 40, 68, 69, 200, 3000], heads=16),
+    "protect_4_16": dict(name="ragged_protect", ctx_lens=[19, 20, 21, 700], heads=16, n_recent=16),
+    "h128_protect": dict(name="ragged_protect", ctx_lens=[1500, 77], heads=128),
+    "tau_gain_extremes": dict(name="v2lite_32k", ctx_lens=[300, 900], tau=0.85, gain=1.2),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_oracle_cache(case):
+    kw = dict(DECODE_CASES[case])
+    prob = workloads.make_problem(kw.pop("name"), **kw)
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    out, lse = run_decode(prob, device_cache_from(oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+    print(f"{case}: out err {err:.2e}, lse err {lerr:.2e}")
+
+
+def test_decode_empty_and_short_contexts():
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[0, 3, 0, 64])
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    out, lse = run_decode(prob, device_cache_from(oc))
+    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+
+
+def test_decode_all_empty():
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[64, 64])
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    out, lse = run_decode(prob, device_cache_from(oc), ctx_lens=[0, 0], max_ctx_len=0)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_decode_split_invariance():
+    """The split grid (sized by the max_ctx_len hint) changes only roundings:
+    P is rounded to fp16 against each wave's running max, so two grids agree
+    to about the fp16 step, and both stay within tolerance of the oracle."""
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[3000, 5000])
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    dc = device_cache_from(oc)
+    prob.block_table = np.pad(prob.block_table, ((0, 0), (0, 2000)))
+    assert rlq.decode_workspace_size(2, 16, 120000) != rlq.decode_workspace_size(2, 16, 5000)
+    out1, lse1 = run_decode(prob, dc)
+    out2, lse2 = run_decode(prob, dc, max_ctx_len=120000)
+    check_decode(out1, lse1, ref_out, ref_lse, prob.ctx_lens)
+    check_decode(out2, lse2, ref_out, ref_lse, prob.ctx_lens)
+    d = (out1 - out2).abs().amax(dim=-1) / out1.abs().amax(dim=-1)
+    assert float(d.max()) < 1e-3
+    assert float((lse1 - lse2).abs().max()) < 1e-4
+
+
+def test_decode_protected_slots_ignore_codes():
+    prob = workloads.make_problem("ragged_protect", ctx_lens=[300, 90], heads=16)
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    dc = device_cache_from(oc)
+    out1, lse1 = run_decode(prob, dc)
+    rng = np.random.default_rng(3)
+    for b, n in enumerate(prob.ctx_lens):
+        for t in list(range(prob.n_sink)) + list(range(n - prob.n_recent, n)):
+            pg, sl = prob.block_table[b, t // 64], t % 64
+            dc.codes[pg, sl] = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, 32, dtype=np.int64).astype(np.int32)).cuda()
+            dc.meta[pg, sl] = torch.from_numpy(rng.standard_normal(8).astype(np.float32) * 1e3).cuda()
+    out2, lse2 = run_decode(prob, dc)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_decode_garbage_beyond_context():
+    """Slots past ctx_len in the last page hold garbage (even NaN); output unchanged."""
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[100, 37])
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    dc = device_cache_from(oc)
+    out1, lse1 = run_decode(prob, dc)
+    for b, n in enumerate(prob.ctx_lens):
+        pg = prob.block_table[b, (n - 1) // 64]
+        dc.meta[pg, n % 64:] = float("nan")
+        dc.rope[pg, n % 64:] = float("nan")
+        dc.codes[pg, n % 64:] = -1
+    out2, lse2 = run_decode(prob, dc)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("case", ["tiny", "protect"])
+def test_end_to_end_append_then_decode(case):
+    """GPU append (Haar rotation on MFMA) + GPU decode vs oracle append + decode."""
+    if case == "tiny":
+        prob = workloads.make_problem("tiny")
+    else:
+        prob = workloads.make_problem("ragged_protect", ctx_lens=[700, 130, 1], heads=32)
+    oc, _ = oracle_cache_for(prob)
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    dc = empty_device_cache(prob)
+    rlq.quantize_append(params_of(prob), dc, dev(prob.k_rope_bits), dev(prob.cu_seqlens),
+                        dev(prob.start_pos), dev(prob.block_table), latent=dev(prob.latent_bits),
+                        rotation=dev(prob.rotation_bits))
+    out, lse = run_decode(prob, dc)
+    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+
+
+def test_decode_invalid_arguments():
+    prob = workloads.make_problem("tiny")
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    dc = device_cache_from(oc)
+    p = params_of(prob)
+    args = (dev(prob.block_table), dev(prob.ctx_lens), 256)
+    q_c = dev(prob.q_c_bits)
+    q_r = dev(prob.q_r_bits)
+    with pytest.raises(ValueError):  # 8 heads: not a multiple of 16
+        rlq.mla_decode(p, dc, q_c[:, :8].contiguous(), q_r[:, :8].contiguous(), 0.1, *args)
+    with pytest.raises(ValueError):  # context beyond the block table
+        rlq.mla_decode(p, dc, q_c, q_r, 0.1, dev(prob.block_table), dev(prob.ctx_lens), 100000)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rlq.RlqError):
+        rlq.mla_decode(p, dc, q_c, q_r, 0.1, *args, workspace=small)
