@@ -137,7 +137,7 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
 int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
                                   size_t *bytes) {
   if (bytes == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16 ||
-      max_ctx_len < 0)
+      max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX)
     return RLQ_EINVAL;
   *bytes = rlq::decode_workspace_bytes(batch, heads, rlq::plan_splits(batch, heads, max_ctx_len));
   return RLQ_OK;
@@ -152,7 +152,7 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
                    void *workspace, size_t workspace_bytes, void *stream) {
   if (p == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16)
     return RLQ_EINVAL;
-  if (max_ctx_len < 0 || max_pages_per_req < 1 ||
+  if (max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX || max_pages_per_req < 1 ||
       (int64_t)max_ctx_len > (int64_t)max_pages_per_req * RLQ_PAGE)
     return RLQ_EINVAL;
   int st = check_cache(cache, batch);
@@ -185,11 +185,12 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   a.heads = heads;
   a.tokens_per_split = plan.tokens_per_split;
   a.splits = plan.splits;
+  a.prot = ((a.sink != nullptr && a.n_sink > 0) || (a.recent != nullptr && a.n_recent > 0)) ? 1 : 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.gain = p->gain;
   a.level_inner = p->level_inner;
   a.level_outer = p->level_outer;
-  const size_t parts = (size_t)batch * (heads / 16) * plan.splits;
+  const size_t parts = (size_t)batch * (heads / 16) * (plan.splits + a.prot);
   a.part_o = (float *)workspace;
   a.part_ml = a.part_o + parts * rlq::kPartialFloats;
   a.out = out;

@@ -50,6 +50,12 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 // Per-(request, head group, split) partial: 16 heads x 512 latent fp32 in the
 // accumulator's own order, then (max, sum) per head.
 constexpr int kPartialFloats = 16 * RLQ_DC;
+// Upper bound on splits per request (the merge keeps one weight per split).
+constexpr int kMaxSplits = 256;
+// Upper bound on pages per split (their ids are staged in LDS); together with
+// kMaxSplits it bounds the context length at RLQ_MAX_CTX tokens.
+constexpr int kMaxSplitPages = 256;
+static_assert((int64_t)kMaxSplits * kMaxSplitPages * RLQ_PAGE == RLQ_MAX_CTX, "context bound");
 
 struct DecodeArgs {
   const uint32_t *codes;
@@ -67,12 +73,13 @@ struct DecodeArgs {
   int32_t heads;
   int32_t tokens_per_split;
   int32_t splits;
+  int32_t prot;      // 1 if sink/recent buffers are given (one more partial per request)
   float scale_log2;  // sm_scale * log2(e)
   float gain;
   float level_inner;
   float level_outer;
-  float *part_o;   // [B][HG][S][kPartialFloats]
-  float *part_ml;  // [B][HG][S][16][2]
+  float *part_o;   // [B][HG][S+prot][kPartialFloats]
+  float *part_ml;  // [B][HG][S+prot][16][2]
   float *out;      // [B][H][512]
   float *lse;      // [B][H] or null
 };
@@ -81,6 +88,7 @@ struct DecodeArgs {
 struct SplitPlan {
   int32_t tokens_per_split;
   int32_t splits;
+  int32_t prot;      // 1 if sink/recent buffers are given (one more partial per request)
 };
 SplitPlan plan_splits(int32_t batch, int32_t heads, int32_t max_ctx_len);
 size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &plan);

@@ -70,6 +70,7 @@ enum {
 #define RLQ_PAGE 64       /* tokens per cache page                                 */
 #define RLQ_WORDS 32      /* uint32 code words per token (16 codes per word)       */
 #define RLQ_MAX_HEADS 128
+#define RLQ_MAX_CTX 4194304  /* longest context one decode call accepts (tokens)  */
 
 /*
  * Per-layer quantizer parameters, fixed while serving (§3.3).
@@ -182,7 +183,8 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
 /*
  * Workspace (bytes) that rlq_mla_decode needs for this batch, head count and
  * maximum context length: split-KV partials (unnormalised output, running max
- * and sum per split and head).  Errors: RLQ_EINVAL.
+ * and sum per split and head).  Errors: RLQ_EINVAL (also for max_ctx_len
+ * above RLQ_MAX_CTX).
  */
 int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
                                   size_t *bytes);
@@ -206,14 +208,15 @@ int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_
  *   sm_scale       softmax scale
  *   block_table    device int32 [batch][max_pages_per_req]
  *   ctx_lens       device int32 [batch], 0 <= ctx_lens[b] <= max_ctx_len
- *   max_ctx_len    host bound on ctx_lens (sizes the split grid)
+ *   max_ctx_len    host bound on ctx_lens (sizes the split grid), at most
+ *                  RLQ_MAX_CTX
  *   out            device fp32 [batch][heads][512]
  *   lse            device fp32 [batch][heads] natural-log LSE, or NULL
  *   workspace      device scratch of at least rlq_mla_decode_workspace_size()
  *                  bytes; its contents need no initialisation
  * ctx_lens[b] = 0 gives out = 0 and lse = -inf.
  * Errors: RLQ_EINVAL (pointers, heads, batch, max_ctx_len beyond the block
- * table), RLQ_ENOSPC, RLQ_EUNSUPPORTED, RLQ_EHIP.
+ * table or above RLQ_MAX_CTX), RLQ_ENOSPC, RLQ_EUNSUPPORTED, RLQ_EHIP.
  */
 int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
                    const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
