@@ -26,9 +26,10 @@
  * ---------------------------------
  *  - Pointers marked "device" are HIP device pointers; the caller allocates
  *    and owns them.  The library allocates nothing, keeps no pointer after a
- *    call returns, holds no global state, and never synchronizes: work is
- *    enqueued on `stream` and the caller keeps every buffer alive until the
- *    stream has completed it.
+ *    call returns and never synchronizes: work is enqueued on `stream` and the
+ *    caller keeps every buffer alive until the stream has completed it.  Its
+ *    only process-wide state is a per-device "is gfx950" check result and the
+ *    decode kernel's one-time LDS-size attribute, both set on first use.
  *  - Device pointers must be 16-byte aligned and their arrays contiguous in
  *    the layouts given below.
  *  - Each call returns an RLQ_* status.  Host-side validation runs before any
