@@ -4,32 +4,35 @@
 // (read-side rotation folded into the absorbed projections), §4.1 / §A.3
 // (sink and recent tokens kept in BF16), Fig. 1a / Fig. 3a.
 //
-// Split-KV.  Workgroup (split, request, head group) walks a page-aligned
-// token range one 64-token page at a time with 4 waves:
-//  * score phase - wave w owns token tile w (16 tokens) of the page.  Each
-//    lane loads, for one token, two 16-byte runs of code words, the (mean,
-//    scale) pairs of the two groups those words belong to, and 32 bytes of
-//    the RoPE key.  A per-(token, group) table of the four fp16 values
-//    mu + s*g*{-b,-a,+a,+b} (rounded once from fp32) is applied to the codes
-//    with byte permutes (v_perm_b32), giving the fp16 c_hat operand with no
-//    per-coordinate arithmetic.  Scores S^T[token, head] = c_hat.q_c +
-//    k_R.q_R run on MFMA (16x16x32 fp16 content part, 16x16x32 bf16 RoPE
-//    part) in a contraction order chosen so every lane's operand comes
-//    straight from the code words it loaded; the absorbed query is laid out
-//    in the same order once per workgroup.  c_hat also goes to LDS (1 KB per
-//    token) and the scores to a small LDS array.
-//  * value phase - after one barrier every wave reads the 64 scores of each
-//    head, updates the online softmax (identical on all waves), and
-//    accumulates O^T[latent, head] += c_hat^T P^T for its own quarter of the
-//    512 latent coordinates, reading c_hat^T with the gfx950 LDS transpose
-//    load (ds_read_b64_tr_b16).  P (times 2^15, to stay in fp16's normal
-//    range) never leaves registers.
-// The last split index of a request (when protection buffers are given)
-// covers the BF16 sink/recent tokens with the same two phases; the other
-// splits mask those tokens out.  A second kernel merges the per-split
-// partials (LSE merge) and restores the natural coordinate order.
+// Split-KV.  Workgroup (split, request, 16-head group) = four wave pairs,
+// one workgroup per CU, two waves per SIMD.  Each pair walks its share of the
+// split in 32-token tiles (two 16-token sub-tiles); wave h of a pair owns
+// latent half h (coordinates of K-steps 8h .. 8h+7):
+//  * score - each lane loads, for one token, 16 bytes of code words, the
+//    (mean, scale) of the group they belong to and 16 bytes of the RoPE key.
+//    A per-(token, group) table of the four fp16 values mu + s*g*{-b,-a,+a,+b}
+//    (rounded once from fp32) is applied to the codes with byte permutes
+//    (v_perm_b32), giving the fp16 c_hat operand with no per-coordinate
+//    arithmetic.  Partial scores S^T[token, head] over the wave's half run on
+//    MFMA (16x16x32 fp16 content part, 16x16x32 bf16 RoPE part) in a
+//    contraction order chosen so every lane's operand comes straight from the
+//    code words it loaded; the absorbed query is laid out in the same order
+//    once per workgroup.  c_hat also goes to the wave's LDS region.
+//  * exchange - the two partial scores meet in LDS slots that a reader marks
+//    empty again (kPoison), so no barrier is needed; both waves run the same
+//    lazy online softmax on the full scores.
+//  * value - O^T[latent, head] += c_hat^T P^T for the wave's half, reading
+//    c_hat^T with the gfx950 LDS transpose load (ds_read_b64_tr_b16); P (fp16,
+//    times 2^kBias) never leaves registers.
+// Tiles are software-pipelined: the value product of tile i-1 runs inside the
+// decode loop of tile i.  The pairs of a workgroup merge through LDS at the
+// end; a protected-token kernel covers the BF16 sink/recent tokens, and a
+// merge kernel combines the per-split partials (LSE merge) and restores the
+// natural coordinate order.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "rlq_internal.h"
 
@@ -42,14 +45,28 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kPageTok = 64;                       // tokens per iteration (one page)
-constexpr int kTileBytes = kTile * RLQ_DC * 2;     // 16 KB fp16 c_hat per 16-token tile
-constexpr int kChatBytes = 4 * kTileBytes;         // 64 KB per page
-constexpr int kScoreBytes = 4 * 64 * 16;           // 4 tiles x 64 lanes x f4 scores
-constexpr int kPBytes = 4 * 64 * 8;                // 4 tiles x 64 lanes x 4 fp16 P
-constexpr int kLdsBytes = kChatBytes + kScoreBytes + kPBytes + 4 * kMaxSplitPages;
-// Workgroups resident at once: 2 per CU (LDS: 2 x 71 KB of 160 KB) x 256 CUs.
-constexpr int kResidentWorkgroups = 512;
+constexpr int kPageTok = 64;                        // tokens per page
+constexpr int kWaveTok = 32;                        // tokens per tile
+constexpr int kSubBytes = kTile * (RLQ_DC / 2) * 2; // 8 KB: fp16 c_hat half of 16 tokens
+constexpr int kWaveBytes = 2 * kSubBytes;           // 16 KB of c_hat per wave
+constexpr int kPairs = kDecodeWaves / 2;           // wave pairs per workgroup
+constexpr int kChatBytes = kDecodeWaves * kWaveBytes;  // 128 KB
+constexpr int kXchBytes = kPairs * 2 * 2 * 2 * 64 * 16;  // [pair][parity][half][sub-tile] scores
+constexpr int kLdsBytes = kChatBytes + kXchBytes;      // 160 KB: one workgroup per CU
+constexpr int kQRow = RLQ_DC + 8;  // staged query row (halfs), padded against bank conflicts
+static_assert(16 * kQRow * 2 <= kChatBytes, "query staging fits");
+// Workgroups resident at once: one per CU x 256 CUs.
+constexpr int kResidentWorkgroups = 256;
+// Lazy online softmax: the running max m is raised only when a tile's max
+// exceeds it by more than kLazy (log2 units); P = 2^(s - m + kBias) then
+// stays at most 2^15, inside fp16's range.
+constexpr float kLazy = 8.f;
+constexpr float kBias = 15.f - kLazy;
+// Partial-score exchange between the two waves of a pair: an empty slot holds
+// this NaN pattern (no partial score of finite inputs is NaN); a reader polls
+// at most kSpinLimit times before going on.
+constexpr uint32_t kPoison = 0x7fbadbadu;
+constexpr int kSpinLimit = 1 << 16;
 
 // Contraction order of the content coordinates (shared by the query layout,
 // the code decoding, the LDS layout and the output mapping).  K-step k
@@ -66,10 +83,13 @@ __device__ __host__ constexpr int coord_of(int k, int g, int j) {
 }
 
 // LDS slot (16 bytes) of token row r written by lane group g at K-step k.
-// The xor keeps both the 16-byte writes and the transposed 8-byte reads of
-// the value phase free of bank conflicts.
+// LDS has 64 four-byte banks (256 bytes per cycle): a 16-byte write serves 16
+// lanes per cycle, an 8-byte transposed read 32 lanes.  The xor moves odd
+// K-steps to the other 128-byte half of each 256-byte window, so the 32 lanes
+// of a transposed read (tokens 0-7 of one writer lane group, K-steps 2p and
+// 2p+1, both 8-byte halves) cover all 64 banks once.
 __device__ __host__ constexpr int chat_slot(int k, int g, int r) {
-  return (16 * g + r) ^ (4 * (k & 1));
+  return (16 * g + r) ^ (8 * (k & 1));
 }
 
 // Value tile jp (0..31) holds, in row m = 4q + e (q, e in 0..3), the latent
@@ -147,26 +167,32 @@ __device__ inline u4 convert8(const u4 &w0, const u4 &w1, int h) {
   return r;
 }
 
-// What one lane loads for its token of the current page.
+// What one lane loads for its token of one 16-token sub-tile, for the latent
+// half h of its wave (K-steps 8h .. 8h+7 and RoPE K-step h).
+struct SubLoad {
+  u4 cw;          // code words [4 q0 + 8h, 4 q0 + 8h + 4)
+  float mu, sd;   // (mean, scale) of group 2*(g>>1) + h
+  u4 rp;          // RoPE key elements [16g + 8h, 16g + 8h + 8)
+};
+// A wave tile: 32 consecutive tokens as two 16-token sub-tiles.
 struct TileLoad {
-  u4 cw0, cw1;       // code words [4q0, 4q0+4) and [4q0+8, 4q0+12)
-  float2 mu, sd;     // (mean, scale) of groups 2*(g>>1) and 2*(g>>1)+1
-  u4 rp0, rp1;       // RoPE key elements [16g, 16g+16)
+  SubLoad s[2];
 };
 
-__device__ inline void load_tile(const DecodeArgs &A, int32_t page, int r16, int g4, int w,
-                                 TileLoad &L) {
+__device__ inline void load_sub(const DecodeArgs &A, int64_t slot, int g4, int h, SubLoad &L) {
   const int q0 = 4 * (g4 >> 1) + (g4 & 1);
-  const int64_t slot = (int64_t)page * RLQ_PAGE + w * kTile + r16;
-  const uint32_t *cw = A.codes + slot * RLQ_WORDS + 4 * q0;
-  L.cw0 = *(const u4 *)cw;
-  L.cw1 = *(const u4 *)(cw + 8);
-  const float *m = A.meta + slot * 8 + 2 * (g4 >> 1);
-  L.mu = *(const float2 *)m;
-  L.sd = *(const float2 *)(m + 4);
-  const uint16_t *rp = A.rope + slot * RLQ_DR + 16 * g4;
-  L.rp0 = *(const u4 *)rp;
-  L.rp1 = *(const u4 *)(rp + 8);
+  L.cw = *(const u4 *)(A.codes + slot * RLQ_WORDS + 4 * q0 + 8 * h);
+  const float *m = A.meta + slot * 8 + 2 * (g4 >> 1) + h;
+  L.mu = m[0];
+  L.sd = m[4];
+  L.rp = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
+}
+
+// `first` = cache slot (page * 64 + 0 or 32) of the tile's first token.
+__device__ inline void load_tile(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
+                                 TileLoad &L) {
+  load_sub(A, first + r16, g4, h, L.s[0]);
+  load_sub(A, first + 16 + r16, g4, h, L.s[1]);
 }
 
 struct Protect {
@@ -180,241 +206,394 @@ __device__ inline Protect protect_range(const DecodeArgs &A, int ctx) {
   return p;
 }
 
-__global__ __launch_bounds__(kDecodeThreads, 2) void decode_split_kernel(DecodeArgs A) {
+template <bool V>
+using bool_c = std::integral_constant<bool, V>;
+
+// kProt = false: the ordinary splits (partials prot .. prot + splits - 1 of a
+// request); kProt = true: the BF16 sink/recent tokens (partial 0).
+//
+// Workgroup = kPairs wave pairs (two waves per SIMD); a pair walks its share
+// of the workgroup's tiles.
+// Wave h of a pair owns latent half h: it decodes K-steps 8h .. 8h+7 (and
+// RoPE K-step h) of each tile, so its score accumulator holds a partial sum;
+// the two partials are exchanged through LDS (no barrier: see kPoison) and both
+// waves run the same online softmax on the full scores.  The value product of
+// wave h covers latent half h, whose c_hat it wrote to its own LDS region.
+template <bool kProt>
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // Grid x: [protected-token workgroup if any] then the ordinary splits, so
-  // the short protected workgroups are dispatched first.
-  const int part = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
-  const int sp = part - A.prot;
+  const int b = blockIdx.y, hg = blockIdx.z;
+  const int sp = kProt ? -1 : (int)blockIdx.x;
+  const int part = kProt ? 0 : A.prot + sp;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = wave & 1, pr = wave >> 1;  // latent half, pair
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int HG = A.heads >> 4;
   const int ctx = A.ctx_lens[b];
-  const Protect pr = protect_range(A, ctx);
-  const bool prot_wg = sp < 0;  // the BF16 sink/recent tokens
-  // Token index range of this workgroup: positions for ordinary splits,
-  // indices into the protected list for the protected one.
+  const Protect pr_ = protect_range(A, ctx);
+  // Token range of this workgroup: positions for ordinary splits, indices
+  // into the protected list (sink positions, then recent positions) for the
+  // protected one.
   int t_begin, t_end;
-  if (prot_wg) {
+  if (kProt) {
     t_begin = 0;
-    t_end = pr.ns + pr.nr;
+    t_end = pr_.ns + pr_.nr;
   } else {
     t_begin = sp * A.tokens_per_split;
     t_end = min(ctx, t_begin + A.tokens_per_split);
   }
-  const int u_lo = pr.ns, u_hi = ctx - pr.nr;  // unprotected positions
+  const int u_lo = pr_.ns, u_hi = ctx - pr_.nr;  // unprotected positions
 
-  // ---- absorbed query of 16 heads, staged through LDS into operand order.
+  // Tiles of the workgroup; every pair runs the same number of iterations,
+  // tiles past the range are fully masked.
+  const int n_tiles = t_end > t_begin ? (t_end - t_begin + kWaveTok - 1) / kWaveTok : 0;
+  const int n_iter = (n_tiles + kPairs - 1) / kPairs;
+  const int tile0 = pr * n_iter;
+  // Page ids of the workgroup's range in VGPRs (lane l of register c holds
+  // page p_first + 64c + l): a tile's loads need no memory access for them.
+  const int p_first = t_begin >> 6;
+  const int n_pages = kProt ? 0 : (n_tiles + 1) >> 1;
+  int32_t pid_v[kMaxSplitPages / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
+    const int i = 64 * c + lane;
+    pid_v[c] = i < n_pages ? A.block_table[(int64_t)b * A.max_pages + p_first + i] : 0;
+  }
+  auto page_id = [&](int i) -> int32_t {  // i wave-uniform, < n_pages
+    int32_t v = __builtin_amdgcn_readlane(pid_v[0], i & 63);
+#pragma unroll
+    for (int c = 1; c < kMaxSplitPages / 64; ++c)
+      if ((i >> 6) == c) v = __builtin_amdgcn_readlane(pid_v[c], i & 63);
+    return v;
+  };
+  const int last = n_tiles - 1;
+  auto tile_slot = [&](int i) -> int64_t {  // i = pair-local tile index
+    const int c = t_begin + kWaveTok * min(tile0 + i, last);
+    return (int64_t)page_id((c >> 6) - p_first) * RLQ_PAGE + (c & 63);
+  };
+  // The first two tiles' loads go out before the query staging, so their
+  // latency overlaps it.
+  TileLoad b0, b1;
+  if (!kProt && n_iter > 0) {
+    load_tile(A, tile_slot(0), r16, g4, h, b0);
+    load_tile(A, tile_slot(1), r16, g4, h, b1);
+  }
+
+  // ---- absorbed query of 16 heads, staged through LDS into operand order;
+  // wave h keeps K-steps 8h .. 8h+7 and RoPE K-step h.
   {
     const uint16_t *qsrc = A.q_c + ((int64_t)b * A.heads + hg * 16) * RLQ_DC;
     for (int c = threadIdx.x; c < 16 * RLQ_DC / 8; c += kDecodeThreads)
-      *(u4 *)(smem + 16 * c) = *(const u4 *)(qsrc + 8 * c);
+      *(u4 *)(smem + 2 * kQRow * (c >> 6) + 16 * (c & 63)) = *(const u4 *)(qsrc + 8 * c);
   }
   __syncthreads();
-  half8 qB[16];
+  half8 qB[8];
   {
-    const uint16_t *qs = (const uint16_t *)smem + r16 * RLQ_DC;
+    const uint16_t *qs = (const uint16_t *)smem + r16 * kQRow;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 8; ++k)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        qB[k][j] = (_Float16)bf16_to_f32(qs[coord_of(k, g4, j)]);
+        qB[k][j] = (_Float16)bf16_to_f32(qs[coord_of(8 * h + k, g4, j)]);
   }
-  bf16x8 qrB[2];
-  {
-    const uint16_t *qr = A.q_r + ((int64_t)b * A.heads + hg * 16 + r16) * RLQ_DR + 16 * g4;
-    qrB[0] = __builtin_bit_cast(bf16x8, *(const u4 *)qr);
-    qrB[1] = __builtin_bit_cast(bf16x8, *(const u4 *)(qr + 8));
+  const bf16x8 qrB = __builtin_bit_cast(
+      bf16x8, *(const u4 *)(A.q_r + ((int64_t)b * A.heads + hg * 16 + r16) * RLQ_DR + 16 * g4 + 8 * h));
+  // Exchange slots of partial scores, [pair][parity][half][sub-tile][64 lanes].
+  // A slot holding kPoison in any element is empty: the reader re-poisons a
+  // slot after consuming it, so readiness needs no flag and no barrier.
+  f4 *xch = (f4 *)(smem + kChatBytes);
+  auto xch_at = [&](int i, int half) -> f4 * { return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64; };
+  const f4 poison = __builtin_bit_cast(f4, u4{kPoison, kPoison, kPoison, kPoison});
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    xch_at(par, h)[lane] = poison;
+    xch_at(par, h)[64 + lane] = poison;
   }
   __syncthreads();
 
   float m_run = kNegInf, l_run = 0.f;
-  f4 O[8];
+  f4 O[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) O[i] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 16; ++i) O[i] = f4{0.f, 0.f, 0.f, 0.f};
+  half8 PB = {};  // P of the previous tile: B operand of the value product
 
-  // Transposed-read offset of this lane in the value phase: lane p = r16 of
-  // lane group g4 supplies token row 4*g4 + p/4 and coordinates q = p % 4.
+  unsigned char *wl = smem + wave * kWaveBytes;  // this wave's c_hat (latent half h)
+  // Transposed-read offset of this lane: lane p = r16 of lane group g4 supplies
+  // token row 4*g4 + p/4 of each sub-tile and coordinates q = p % 4.
   const int va = (r16 & 3) >> 1;
-  const int vrd = 1024 * va + 16 * ((4 * g4 + (r16 >> 2)) ^ (4 * va)) + 8 * (r16 & 1);
-  f4 *score_lds = (f4 *)(smem + kChatBytes);
-  u2 *p_lds = (u2 *)(smem + kChatBytes + kScoreBytes);
+  const int vrd = 1024 * va + 16 * ((4 * g4 + (r16 >> 2)) ^ (8 * va)) + 8 * (r16 & 1);
 
-  auto page_of = [&](int t) -> int32_t {
-    return A.block_table[(int64_t)b * A.max_pages + (t >> 6)];
-  };
-  // Page ids of this split, staged once in LDS so that the loads of a page
-  // never wait on a block-table read.
-  const int p_first = t_begin >> 6;
-  const int n_pages = prot_wg ? 0 : (t_end - t_begin + kPageTok - 1) / kPageTok;
-  int32_t *pid_lds = (int32_t *)(smem + kChatBytes + kScoreBytes + kPBytes);
-  for (int i = threadIdx.x; i < n_pages; i += kDecodeThreads)
-    pid_lds[i] = A.block_table[(int64_t)b * A.max_pages + p_first + i];
-  __syncthreads();
-  auto pid_at = [&](int n) -> int32_t { return __builtin_amdgcn_readfirstlane(pid_lds[n]); };
+  // Tile pipeline.  Step i (pair-local tile index) runs, in program order:
+  //   part 1  - transposed reads of tile i-1's K-step pair 0 into registers,
+  //             decode + partial scores of tile i's K-step pair 0 (its c_hat
+  //             overwrites those slots: LDS operations of a wave run in order);
+  //   softmax - barrier, the partner's partial scores of tile i-1, online
+  //             softmax of tile i-1 -> P;
+  //   part 2  - value product O^T += c_hat^T P^T of tile i-1 (pair 0 from
+  //             registers, pairs 1..3 read just before tile i overwrites
+  //             them), decode + partial scores of tile i's pairs 1..3, RoPE
+  //             part, own partial scores of tile i to the exchange buffer.
+  // The partner's partial of tile i-1 was written a whole step earlier, so the
+  // barrier rarely waits, and the exponentials share a basic block with the
+  // decode of tile i.
+  f4 acc_prev[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 
-  // One page: score phase on tile `wave`, barrier, value phase, barrier.
-  auto process_page = [&](const TileLoad &cur, int c0) {
-    const int trow = c0 + wave * kTile + r16;  // operand row of this lane
-    unsigned char *tl = smem + wave * kTileBytes;
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    if (!prot_wg) {
-      const bool valid = trow < t_end && trow >= u_lo && trow < u_hi;
-      const Lut la = make_lut(cur.mu.x, cur.sd.x, A.gain, A.level_inner, A.level_outer, valid);
-      const Lut lb = make_lut(cur.mu.y, cur.sd.y, A.gain, A.level_inner, A.level_outer, valid);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const u4 &run = (k < 8) ? cur.cw0 : cur.cw1;
-        const u4 av = decode8(run[(k >> 1) & 3], k & 1, (k < 8) ? la : lb);
-        *(u4 *)(tl + k * 1024 + 16 * chat_slot(k, g4, r16)) = av;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), qB[k], acc, 0, 0, 0);
-        // Keep each decoded operand's live range to its own K-step.
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.rp0), qrB[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.rp1), qrB[1], acc, 0, 0, 0);
+  // Online softmax of the pair's tile i (partial scores of this wave in
+  // acc_prev).  The running max moves only when a tile exceeds it by more
+  // than kLazy (log2 units), so O is rescaled rarely; P = 2^(s - m + kBias)
+  // stays below 2^15.
+  auto softmax = [&](const f4 &o0, const f4 &o1, int c0, int vlo, int vhi) {
+    // Full scores = own partial + partner's partial (the same sum, in the
+    // same order, on both waves of the pair).
+    f4 sc[2];
+    sc[0] = h == 0 ? acc_prev[0] + o0 : o0 + acc_prev[0];
+    sc[1] = h == 0 ? acc_prev[1] + o1 : o1 + acc_prev[1];
+    // sc[st][j] = score of token c0 + 16*st + 4*g4 + j, head r16.
+    if (c0 >= vlo && c0 + kWaveTok <= vhi) {
+      sc[0] *= A.scale_log2;
+      sc[1] *= A.scale_log2;
     } else {
-      // Protected list index v -> position and BF16 source row.
-      const bool valid = trow < t_end;
-      const int pos = (trow < pr.ns) ? trow : (ctx - pr.nr + (trow - pr.ns));
-      const uint16_t *row = nullptr;
-      if (valid)
-        row = (trow < pr.ns) ? A.sink + ((int64_t)b * A.n_sink + pos) * RLQ_DC
-                             : A.recent + ((int64_t)b * A.n_recent + pos % A.n_recent) * RLQ_DC;
-      const int q0 = 4 * (g4 >> 1) + (g4 & 1);
-      u4 rp0 = u4{0, 0, 0, 0}, rp1 = u4{0, 0, 0, 0};
-      if (valid) {
-        const int64_t slot = (int64_t)page_of(pos) * RLQ_PAGE + (pos & 63);
-        rp0 = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4);
-        rp1 = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8);
-      }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        u4 av = u4{0, 0, 0, 0};
-        if (valid) {
-          const int word = 4 * (q0 + 2 * (k >> 3)) + ((k >> 1) & 3);
-          const u4 w0 = *(const u4 *)(row + 16 * word);
-          const u4 w1 = *(const u4 *)(row + 16 * word + 8);
-          av = convert8(w0, w1, k & 1);
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = c0 + 16 * st + 4 * g4 + j;
+          sc[st][j] = (t >= vlo && t < vhi) ? sc[st][j] * A.scale_log2 : kNegInf;
         }
-        *(u4 *)(tl + k * 1024 + 16 * chat_slot(k, g4, r16)) = av;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), qB[k], acc, 0, 0, 0);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp0), qrB[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp1), qrB[1], acc, 0, 0, 0);
     }
-    // acc[i] = score of token row 4*g4 + i of tile `wave`, head r16.
-    const int vlo = prot_wg ? 0 : u_lo;
-    const int vhi = prot_wg ? t_end : min(t_end, u_hi);
-    if (c0 >= vlo && c0 + kPageTok <= vhi) {
-      acc *= A.scale_log2;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = c0 + wave * kTile + 4 * g4 + i;
-        acc[i] = (t >= vlo && t < vhi) ? acc[i] * A.scale_log2 : kNegInf;
-      }
-    }
-    score_lds[wave * 64 + lane] = acc;
-    __syncthreads();
-
-    // ---------------- softmax: all waves agree on the running max; each
-    // wave exponentiates its own tile and shares fp16 P through LDS.
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f4 sv = score_lds[t * 64 + lane];
-      mx = fmaxf(mx, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-    }
-    mx = max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new > m_run) {  // identical on all lanes of a head
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+    float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mt = max_over_groups(mt);
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) O[i] *= alpha;
+      for (int j = 0; j < 16; ++j) O[j] *= alpha;
       m_run = m_new;
     }
-    // P carries 2^15 (fp16 headroom); while no finite score has been seen the
-    // clamp keeps exp2(-inf - mb) at 0 instead of NaN.
-    const float mb = fmaxf(m_run, -1e30f) - 15.f;
-    {
-      const half2v p01 = __builtin_convertvector(
-          (float2v){__builtin_amdgcn_exp2f(acc[0] - mb), __builtin_amdgcn_exp2f(acc[1] - mb)}, half2v);
-      const half2v p23 = __builtin_convertvector(
-          (float2v){__builtin_amdgcn_exp2f(acc[2] - mb), __builtin_amdgcn_exp2f(acc[3] - mb)}, half2v);
-      l_run = __builtin_amdgcn_fdot2(p01, (half2v){1.0f16, 1.0f16}, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(p23, (half2v){1.0f16, 1.0f16}, l_run, false);
-      p_lds[wave * 64 + lane] = u2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    }
-    __syncthreads();
-    half8 PB[2];
+    // While no finite score has been seen the clamp keeps exp2(-inf - mb) at
+    // 0 instead of NaN.
+    const float mb = fmaxf(m_run, -1e30f) - kBias;
+    half2v ph[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u2 a = p_lds[(2 * kk) * 64 + lane];
-      const u2 c = p_lds[(2 * kk + 1) * 64 + lane];
-      PB[kk] = __builtin_bit_cast(half8, u4{a[0], a[1], c[0], c[1]});
+    for (int st = 0; st < 2; ++st) {
+      ph[2 * st] = __builtin_convertvector(
+          (float2v){__builtin_amdgcn_exp2f(sc[st][0] - mb), __builtin_amdgcn_exp2f(sc[st][1] - mb)}, half2v);
+      ph[2 * st + 1] = __builtin_convertvector(
+          (float2v){__builtin_amdgcn_exp2f(sc[st][2] - mb), __builtin_amdgcn_exp2f(sc[st][3] - mb)}, half2v);
     }
 #pragma unroll
-    for (int jl = 0; jl < 8; ++jl) {
-      const int jp = 8 * wave + jl;
-      const int cofs = 2048 * (jp >> 2) + 256 * (jp & 3);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const unsigned char *base = smem + (2 * kk) * kTileBytes + cofs + vrd;
-        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)base);
-        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + kTileBytes));
-        const half8 av = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[jl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, PB[kk], O[jl], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+    for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2(ph[j], (half2v){1.0f16, 1.0f16}, l_run, false);
+    PB = __builtin_bit_cast(half8, u4{__builtin_bit_cast(uint32_t, ph[0]), __builtin_bit_cast(uint32_t, ph[1]),
+                                      __builtin_bit_cast(uint32_t, ph[2]), __builtin_bit_cast(uint32_t, ph[3])});
   };
 
-  if (prot_wg) {
-    TileLoad none{};
-    for (int c0 = t_begin; c0 < t_end; c0 += kPageTok) process_page(none, c0);
+  auto slot_full = [&](const f4 &a, const f4 &c) -> bool {
+    bool empty = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      empty |= (__float_as_uint(a[j]) == kPoison) | (__float_as_uint(c[j]) == kPoison);
+    return __builtin_amdgcn_ballot_w64(empty) == 0;
+  };
+
+  auto tr_pair = [&](int p, half8 (&av)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned char *base = wl + 2048 * p + 256 * q + vrd;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)base);
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + kSubBytes));
+      av[q] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto value_pair = [&](int p, const half8 (&av)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      O[4 * p + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[q], PB, O[4 * p + q], 0, 0, 0);
+  };
+
+  // kScore: tile i is new (decode + partial scores); kValue: tile i-1 gets its
+  // softmax and value product.
+  auto step = [&](auto score_c, auto value_c, auto &&dec, const u4 (&rp)[2], int i, int c0_prev,
+                  int vlo, int vhi) {
+    constexpr bool kScore = decltype(score_c)::value;
+    constexpr bool kValue = decltype(value_c)::value;
+    f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    auto score_pair = [&](int p) {
+#pragma unroll
+      for (int kl = 2 * p; kl < 2 * p + 2; ++kl)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const u4 v = dec(kl, st);
+          *(u4 *)(wl + st * kSubBytes + kl * 1024 + 16 * chat_slot(kl, g4, r16)) = v;
+          acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), qB[kl], acc[st], 0, 0, 0);
+        }
+    };
+    half8 av0[4];
+    f4 o0, o1;
+    f4 *other = xch_at(i - 1, h ^ 1);
+    if constexpr (kValue) {
+      // The partner's partial of tile i-1 (written at the end of its
+      // previous step); the read is issued before part 1 so that waiting for
+      // it does not wait for part 1's LDS traffic.
+      o0 = other[lane];
+      o1 = other[64 + lane];
+      tr_pair(0, av0);
+    }
+    if constexpr (kScore) score_pair(0);
+    if constexpr (kValue) {
+      if (!slot_full(o0, o1)) {
+        // Rare: the partner is behind.  Poll with a bound, so a wave can never
+        // wait forever.
+        for (int n = 0; n < kSpinLimit; ++n) {
+          __builtin_amdgcn_s_sleep(2);
+          asm volatile("" ::: "memory");
+          o0 = other[lane];
+          o1 = other[64 + lane];
+          if (slot_full(o0, o1)) break;
+        }
+      }
+      other[lane] = poison;
+      other[64 + lane] = poison;
+      softmax(o0, o1, c0_prev, vlo, vhi);
+      value_pair(0, av0);
+    }
+#pragma unroll
+    for (int p = 1; p < 4; ++p) {
+      half8 av[4];
+      if constexpr (kValue) tr_pair(p, av);
+      if constexpr (kScore) score_pair(p);
+      if constexpr (kValue) value_pair(p, av);
+    }
+    if constexpr (kScore) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
+      f4 *mine = xch_at(i, h);
+      mine[lane] = acc[0];
+      mine[64 + lane] = acc[1];
+      acc_prev[0] = acc[0];
+      acc_prev[1] = acc[1];
+    }
+  };
+  auto no_dec = [](int, int) -> u4 { return u4{0, 0, 0, 0}; };
+  const u4 no_rp[2] = {};
+
+  if constexpr (!kProt) {
+    const int vlo = u_lo, vhi = u_hi < t_end ? u_hi : t_end;
+    auto c0_of = [&](int i) { return t_begin + kWaveTok * (tile0 + i); };
+    auto run = [&](auto value_c, const TileLoad &cur, int i) {
+      const int c0 = c0_of(i);
+      Lut lut[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int t = c0 + 16 * st + r16;
+        lut[st] = make_lut(cur.s[st].mu, cur.s[st].sd, A.gain, A.level_inner, A.level_outer,
+                           t >= vlo && t < vhi);
+      }
+      auto dec = [&](int kl, int st) -> u4 {
+        return decode8(cur.s[st].cw[(kl >> 1) & 3], kl & 1, lut[st]);
+      };
+      const u4 rp[2] = {cur.s[0].rp, cur.s[1].rp};
+      step(bool_c<true>{}, value_c, dec, rp, i, c0_of(i - 1), vlo, vhi);
+    };
+    if (n_iter > 0) {
+      // Two load buffers used alternately: the loads of tile i+1 are in
+      // flight while tile i is processed.  Loads are issued unconditionally
+      // (past the end the last tile is loaded again, from L2) so the loop
+      // body has one straight path and the wait counts cover only the buffer
+      // being consumed.
+      run(bool_c<false>{}, b0, 0);
+      for (int i = 1; i < n_iter; i += 2) {
+        load_tile(A, tile_slot(i + 1), r16, g4, h, b0);
+        run(bool_c<true>{}, b1, i);
+        if (i + 1 >= n_iter) break;
+        load_tile(A, tile_slot(i + 2), r16, g4, h, b1);
+        run(bool_c<true>{}, b0, i + 1);
+      }
+      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, c0_of(n_iter - 1), vlo, vhi);
+    }
   } else {
-    // Two load buffers used alternately: the loads of page n+1 are in flight
-    // while page n is processed, with no register copies between them.
-    // Three load buffers in a ring: while page n is processed the loads of
-    // pages n+1 and n+2 are in flight.  Loads are issued unconditionally (past
-    // the end the last page is loaded again, from L2) so the loop body has one
-    // straight path and the compiler's wait counts cover only the buffer
-    // being consumed.
-    TileLoad buf0, buf1, buf2;
-    const int last = n_pages - 1;
-    if (n_pages > 0) {
-      load_tile(A, pid_at(0), r16, g4, wave, buf0);
-      load_tile(A, pid_at(min(1, last)), r16, g4, wave, buf1);
+    // Protected list index v -> position and BF16 source row.
+    const int q0 = 4 * (g4 >> 1) + (g4 & 1);
+    for (int i = 0; i < n_iter; ++i) {
+      const int c0 = kWaveTok * (tile0 + i);
+      const uint16_t *row[2] = {nullptr, nullptr};
+      u4 rp[2] = {};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int v = c0 + 16 * st + r16;
+        if (v < t_end) {
+          const int pos = (v < pr_.ns) ? v : (ctx - pr_.nr + (v - pr_.ns));
+          row[st] = (v < pr_.ns) ? A.sink + ((int64_t)b * A.n_sink + pos) * RLQ_DC
+                                 : A.recent + ((int64_t)b * A.n_recent + pos % A.n_recent) * RLQ_DC;
+          const int64_t slot =
+              (int64_t)A.block_table[(int64_t)b * A.max_pages + (pos >> 6)] * RLQ_PAGE + (pos & 63);
+          rp[st] = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
+        }
+      }
+      auto dec = [&](int kl, int st) -> u4 {
+        if (row[st] == nullptr) return u4{0, 0, 0, 0};
+        const int word = 4 * (q0 + 2 * h) + ((kl >> 1) & 3);
+        const u4 w0 = *(const u4 *)(row[st] + 16 * word);
+        const u4 w1 = *(const u4 *)(row[st] + 16 * word + 8);
+        return convert8(w0, w1, kl & 1);
+      };
+      if (i == 0)
+        step(bool_c<true>{}, bool_c<false>{}, dec, rp, i, 0, 0, t_end);
+      else
+        step(bool_c<true>{}, bool_c<true>{}, dec, rp, i, c0 - kWaveTok, 0, t_end);
     }
-    for (int n = 0; n < n_pages; n += 3) {
-      load_tile(A, pid_at(min(n + 2, last)), r16, g4, wave, buf2);
-      process_page(buf0, t_begin + n * kPageTok);
-      if (n + 1 >= n_pages) break;
-      load_tile(A, pid_at(min(n + 3, last)), r16, g4, wave, buf0);
-      process_page(buf1, t_begin + (n + 1) * kPageTok);
-      if (n + 2 >= n_pages) break;
-      load_tile(A, pid_at(min(n + 4, last)), r16, g4, wave, buf1);
-      process_page(buf2, t_begin + (n + 2) * kPageTok);
-    }
+    if (n_iter > 0)
+      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, kWaveTok * (tile0 + n_iter - 1), 0, t_end);
   }
 
-  // ---- partial of this workgroup: each wave writes its quarter of O; the
-  // sum of P is spread over the waves (each summed its own tiles).
+  // ---- partial of the workgroup: pairs 1 .. kPairs-1 hand their (max, sum,
+  // O) to pair 0 through LDS; wave h of pair 0 merges latent half h.
   l_run = sum_over_groups(l_run);
-  float *l_lds = (float *)(smem + kChatBytes);  // free after the last barrier
-  if (g4 == 0) l_lds[wave * 16 + r16] = l_run;
-  __syncthreads();
-  const int64_t pidx = ((int64_t)b * HG + hg) * (A.splits + A.prot) + part;
-  f4 *po = (f4 *)(A.part_o + pidx * kPartialFloats);
+  __syncthreads();  // every wave is done with its c_hat region and the exchange
+  float *ml = (float *)(smem + kChatBytes);  // [pair][16 heads][2]
+  if (pr > 0) {
+    if (h == 0 && g4 == 0) {
+      ml[(pr * 16 + r16) * 2] = m_run;
+      ml[(pr * 16 + r16) * 2 + 1] = l_run;
+    }
+    f4 *ol = (f4 *)(smem + ((pr - 1) * 2 + h) * kWaveBytes);
 #pragma unroll
-  for (int jl = 0; jl < 8; ++jl) po[(8 * wave + jl) * 64 + lane] = O[jl];
-  if (wave == 0 && g4 == 0) {
-    const float l_all = (l_lds[r16] + l_lds[16 + r16]) + (l_lds[32 + r16] + l_lds[48 + r16]);
-    A.part_ml[pidx * 32 + 2 * r16] = m_run;
-    A.part_ml[pidx * 32 + 2 * r16 + 1] = l_all;
+    for (int j = 0; j < 16; ++j) ol[j * 64 + lane] = O[j];
+  }
+  __syncthreads();
+  if (pr == 0) {
+    float mv[kPairs], sc[kPairs];
+    mv[0] = m_run;
+    float M = m_run;
+#pragma unroll
+    for (int v = 1; v < kPairs; ++v) {
+      mv[v] = ml[(v * 16 + r16) * 2];
+      M = fmaxf(M, mv[v]);
+    }
+    const float Mc = fmaxf(M, -1e30f);  // 0 weights for empty pairs
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kPairs; ++v) {
+      sc[v] = __builtin_amdgcn_exp2f(mv[v] - Mc);
+      L += sc[v] * (v == 0 ? l_run : ml[(v * 16 + r16) * 2 + 1]);
+    }
+    const int64_t pidx = ((int64_t)b * HG + hg) * (A.splits + A.prot) + part;
+    f4 *po = (f4 *)(A.part_o + pidx * kPartialFloats);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      f4 o = sc[0] * O[j];
+#pragma unroll
+      for (int v = 1; v < kPairs; ++v)
+        o += sc[v] * ((const f4 *)(smem + ((v - 1) * 2 + h) * kWaveBytes))[j * 64 + lane];
+      po[(16 * h + j) * 64 + lane] = o;
+    }
+    if (h == 0 && g4 == 0) {
+      A.part_ml[pidx * 32 + 2 * r16] = M;
+      A.part_ml[pidx * 32 + 2 * r16 + 1] = L;
+    }
   }
 }
 
@@ -485,14 +664,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
     for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
     if (A.lse != nullptr && jp == 0 && lane < 16)
       A.lse[(int64_t)b * A.heads + hg * 16 + lane] =
-          L > 0.f ? (Mh + log2f(L) - 15.f) * 0.69314718055994531f : kNegInf;
+          L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
   }
 }
 
 }  // namespace
 
 SplitPlan plan_splits(int32_t batch, int32_t heads, int32_t max_ctx_len) {
-  // One round of workgroups that fills the GPU exactly: two per CU (256 CUs,
+  // One round of workgroups that fills the GPU exactly: one per CU (256 CUs,
   // LDS-limited), in whole pages, at most kMaxSplits splits per request.
   const int64_t hg = heads / 16;
   const int64_t ctx = max_ctx_len > 0 ? max_ctx_len : 1;
@@ -519,13 +698,20 @@ size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &pla
 hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_split_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
+    for (const void *f : {(const void *)decode_split_kernel<false>, (const void *)decode_split_kernel<true>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   const int hg = a.heads / 16;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.splits + a.prot, batch, hg), dim3(kDecodeThreads),
+  if (a.prot) {
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(1, batch, hg), dim3(kDecodeThreads), kLdsBytes,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.splits, batch, hg), dim3(kDecodeThreads),
                      kLdsBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -45,7 +45,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 // Tokens of one wave iteration and of one score tile.
 constexpr int kChunk = 32;
 constexpr int kTile = 16;
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 // Per-(request, head group, split) partial: 16 heads x 512 latent fp32 in the
 // accumulator's own order, then (max, sum) per head.

@@ -40,6 +40,23 @@ def test_decode_oracle_cache(case):
     print(f"{case}: out err {err:.2e}, lse err {lerr:.2e}")
 
 
+def test_decode_rising_scores_rescale():
+    """Scores that climb by ~10 (log2 units) every 32 tokens, in a sawtooth of
+    period 256: every tile raises the running max past the lazy-rescale
+    threshold, so the rescale of the accumulated output runs on almost every
+    tile, and the softmax mass sits on one token per period."""
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[3000, 777, 4096])
+    pos = np.concatenate([np.arange(n) for n in prob.ctx_lens])
+    ramp = (0.094 * (pos % 256)).astype(np.float32)
+    prob.k_rope_bits = workloads.to_bf16_bits(np.repeat(ramp[:, None], 64, axis=1))
+    prob.q_r_bits = workloads.to_bf16_bits(np.full(prob.q_r_bits.shape, 0.5, np.float32))
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    out, lse = run_decode(prob, device_cache_from(oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+    print(f"rising scores: out err {err:.2e}, lse err {lerr:.2e}")
+
+
 def test_decode_empty_and_short_contexts():
     prob = workloads.make_problem("v2lite_32k", ctx_lens=[0, 3, 0, 64])
     oc, _ = oracle_cache_for(prob, z=z_of(prob))
@@ -57,8 +74,9 @@ def test_decode_all_empty():
 
 def test_decode_split_invariance():
     """The split grid (sized by the max_ctx_len hint) changes only roundings:
-    P is rounded to fp16 against each wave's running max, so two grids agree
-    to about the fp16 step, and both stay within tolerance of the oracle."""
+    P is rounded to fp16 against each wave's running reference max (which may
+    lag the true max by up to 2^8), so two grids agree to a few fp16 steps,
+    and both stay within tolerance of the oracle."""
     prob = workloads.make_problem("v2lite_32k", ctx_lens=[3000, 5000])
     oc, _ = oracle_cache_for(prob, z=z_of(prob))
     ref_out, ref_lse = oracle_decode(prob, oc)
@@ -71,7 +89,7 @@ def test_decode_split_invariance():
     check_decode(out2, lse2, ref_out, ref_lse, prob.ctx_lens)
     d = (out1 - out2).abs().amax(dim=-1) / out1.abs().amax(dim=-1)
     assert float(d.max()) < 1e-3
-    assert float((lse1 - lse2).abs().max()) < 1e-4
+    assert float((lse1 - lse2).abs().max()) < 5e-4
 
 
 def test_decode_protected_slots_ignore_codes():
