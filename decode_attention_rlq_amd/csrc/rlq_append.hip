@@ -4,10 +4,9 @@
 // the per-layer threshold), §A.3 (group 128 with two fp32 statistics, BF16
 // RoPE key, protected tokens keep BF16 content), §4.1 (sink + recent tokens).
 //
-// One workgroup handles 64 consecutive new tokens; wave w owns coordinate
-// group w (128 outputs).  The rotation z^T = R c^T runs on bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation: A = rows of R (M =
-// outputs), B = token latents (N = tokens).  In the accumulator layout each
+// The rotation z^T = R c^T runs on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with
+// fp32 accumulation: A = rows of R (M = outputs of one coordinate group), B =
+// token latents (N = tokens).  In the accumulator layout each
 // lane holds, for one token, outputs 16*mt + 4*(lane/16) + i of every 16-row
 // tile mt, which lets the statistics follow the fixed adjacent-pair tree:
 // two in-lane levels, two cross-lane levels (xor 16, xor 32), three in-lane
@@ -22,7 +21,6 @@
 namespace rlq {
 namespace {
 
-constexpr int kAppTokens = 64;
 // Up to this many new tokens the few-token kernel is used.
 constexpr int64_t kSmallTokens = 4096;
 
@@ -41,6 +39,24 @@ __device__ inline int find_request(const int32_t *cu, int batch, int64_t tok) {
   return lo;
 }
 
+// Value of lane l ^ 32 (resp. l ^ 16) combined with this lane's by v_permlane
+// swaps (no LDS traffic).  Both lanes of a pair get the same bits: the
+// operations used (+, |) are commutative.
+__device__ inline float add_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float add_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline uint32_t or_xor16_32(uint32_t w) {
+  const auto p = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  w = p[0] | p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return q[0] | q[1];
+}
+
 __device__ inline float tree8(const float (&v)[8]) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
@@ -51,19 +67,45 @@ __device__ inline float group_tree_sum(const float (&x)[8][4]) {
   float s16[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    float s4 = (x[mt][0] + x[mt][1]) + (x[mt][2] + x[mt][3]);
-    float s8 = s4 + __shfl_xor(s4, 16, 64);
-    s16[mt] = s8 + __shfl_xor(s8, 32, 64);
+    const float s4 = (x[mt][0] + x[mt][1]) + (x[mt][2] + x[mt][3]);
+    s16[mt] = add_xor32(add_xor16(s4));
   }
   return tree8(s16);
+}
+
+// Where a new token goes: its request, position and cache slot (-1 for
+// tokens past the end).  Resolved before the rotation so that the dependent
+// loads (request search, block table) overlap it.
+struct Dest {
+  int64_t slot;
+  int32_t pos;  // position in the request (contexts stay below 2^31)
+  int32_t b;
+};
+
+__device__ inline Dest resolve(const AppendArgs &a, int64_t tok) {
+  Dest d{-1, 0, 0};
+  if (tok >= a.n_tokens) return d;
+  d.b = find_request(a.cu_seqlens, a.batch, tok);
+  d.pos = a.start_pos[d.b] + (int32_t)(tok - a.cu_seqlens[d.b]);
+  d.slot = (int64_t)a.block_table[(int64_t)d.b * a.max_pages + (d.pos >> 6)] * RLQ_PAGE + (d.pos & 63);
+  return d;
+}
+
+// RoPE key of one token (128 bytes) to its slot.
+__device__ inline void copy_rope_token(const AppendArgs &a, int64_t tok, const Dest &d) {
+  if (d.slot < 0) return;
+  const u4 *src = (const u4 *)(a.k_rope + tok * RLQ_DR);
+  u4 *dst = (u4 *)(a.rope + d.slot * RLQ_DR);
+#pragma unroll
+  for (int c = 0; c < RLQ_DR / 8; ++c) dst[c] = src[c];
 }
 
 // Statistics, codes and stores for one token and one group: z[mt][i] is
 // output 16*mt + 4*kg + i of group G; the four lanes {n, n+16, n+32, n+48}
 // hold the whole group.  All 64 lanes must call it (cross-lane sums).
 __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4], int64_t tok,
-                                    int G, int kg) {
-  const bool valid = tok < a.n_tokens;
+                                    const Dest &dst_tok, int G, int kg) {
+  const bool valid = dst_tok.slot >= 0;
   const float mu = group_tree_sum(z) * 0.0078125f;
   float d[8][4], sq[8][4];
 #pragma unroll
@@ -86,17 +128,11 @@ __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4],
       const uint32_t c = (uint32_t)(x >= -t) + (uint32_t)(x >= 0.f) + (uint32_t)(x >= t);
       byte |= c << (2 * i);
     }
-    uint32_t w = byte << (8 * kg);
-    w |= (uint32_t)__shfl_xor((int)w, 16, 64);
-    w |= (uint32_t)__shfl_xor((int)w, 32, 64);
-    word[mt] = w;
+    word[mt] = or_xor16_32(byte << (8 * kg));
   }
   if (!valid) return;
-
-  const int b = find_request(a.cu_seqlens, a.batch, tok);
-  const int64_t pos = (int64_t)a.start_pos[b] + (tok - a.cu_seqlens[b]);
-  const int32_t page = a.block_table[(int64_t)b * a.max_pages + (pos >> 6)];
-  const int64_t slot = (int64_t)page * RLQ_PAGE + (pos & 63);
+  const int b = dst_tok.b;
+  const int64_t pos = dst_tok.pos, slot = dst_tok.slot;
 
   // Lane group kg stores code words 2kg, 2kg+1 of this group.
   *(u2 *)(a.codes + slot * RLQ_WORDS + 8 * G + 2 * kg) = u2{word[2 * kg], word[2 * kg + 1]};
@@ -109,8 +145,9 @@ __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4],
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) *(f4 *)(dst + 16 * mt) = f4{z[mt][0], z[mt][1], z[mt][2], z[mt][3]};
   }
-  const int64_t new_len = (int64_t)a.start_pos[b] + (a.cu_seqlens[b + 1] - a.cu_seqlens[b]);
   uint16_t *prot[2] = {nullptr, nullptr};
+  if (a.sink == nullptr && a.recent == nullptr) return;
+  const int64_t new_len = (int64_t)a.start_pos[b] + (a.cu_seqlens[b + 1] - a.cu_seqlens[b]);
   if (a.sink != nullptr && pos < a.n_sink)
     prot[0] = a.sink + ((int64_t)b * a.n_sink + pos) * RLQ_DC;
   if (a.recent != nullptr && pos >= new_len - a.n_recent)
@@ -128,95 +165,118 @@ __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4],
   }
 }
 
-// RoPE key copy of tokens [tok0, tok0 + count): 16 bytes per thread step.
-__device__ inline void copy_rope(const AppendArgs &a, int64_t tok0, int count, int tid, int nthreads) {
-  for (int c = tid; c < count * 8; c += nthreads) {
-    const int64_t tok = tok0 + (c >> 3);
-    if (tok >= a.n_tokens) continue;
-    const int b = find_request(a.cu_seqlens, a.batch, tok);
-    const int64_t pos = (int64_t)a.start_pos[b] + (tok - a.cu_seqlens[b]);
-    const int32_t page = a.block_table[(int64_t)b * a.max_pages + (pos >> 6)];
-    const int64_t slot = (int64_t)page * RLQ_PAGE + (pos & 63);
-    *(u4 *)(a.rope + slot * RLQ_DR + 8 * (c & 7)) = *(const u4 *)(a.k_rope + tok * RLQ_DR + 8 * (c & 7));
-  }
-}
+// Bulk path: one persistent workgroup per CU.  Workgroup (G, slot) keeps the
+// 128 rows of R for coordinate group G in LDS (128 KB) and streams 512-token
+// tiles through eight waves of 64 tokens; the K loop needs no barrier.  The
+// rotation z^T = R c^T: A = rows of R from LDS (M = outputs), B = latents
+// straight from memory (N = tokens), fp32 accumulation.
+constexpr int kBulkWaves = 8;
+constexpr int kBulkTile = 64 * kBulkWaves;           // tokens per workgroup pass
+constexpr int kBulkSlots = 8;                        // workgroups per (XCD, group)
+constexpr int kBulkGrid = 8 * RLQ_NGROUPS * kBulkSlots;  // 256: one per CU
+constexpr int kRSlice = RLQ_GROUP * 32 * 2;          // 8 KB: 128 rows x 32 K
+constexpr int kRBytes = (RLQ_DC / 32) * kRSlice;     // 128 KB
 
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char rs[];
   const int lane = threadIdx.x & 63;
-  const int G = threadIdx.x >> 6;  // coordinate group of this wave
+  const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int kg = lane >> 4;
-  const int64_t tile0 = (int64_t)blockIdx.x * kAppTokens;
+  // Workgroups are dealt to the 8 XCDs round-robin: the four group
+  // workgroups of one slot share an XCD and walk the same tiles, so three of
+  // them read each tile's latents from that XCD's L2.
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int G = j & 3, slot = j >> 2;
+  // 16-byte chunk c (K 8c .. 8c+7) of row r in K-slice k; the xor spreads the
+  // operand reads of 16 consecutive rows over distinct banks.
+  auto chunk = [](int k, int r, int c) { return k * kRSlice + 64 * r + 16 * (c ^ ((r >> 2) & 3)); };
+  if (a.latent_rot == nullptr) {
+    for (int i = threadIdx.x; i < RLQ_GROUP * RLQ_DC / 8; i += 64 * kBulkWaves) {
+      const int r = i >> 6, kc = i & 63;  // row, 8-element chunk along K
+      *(u4 *)(rs + chunk(kc >> 2, r, kc & 3)) =
+          *(const u4 *)(a.rotation + (size_t)(G * RLQ_GROUP + r) * RLQ_DC + 8 * kc);
+    }
+    __syncthreads();
+  }
 
-  f4 acc[4][8];
+  const int64_t n_tiles = (a.n_tokens + kBulkTile - 1) / kBulkTile;
+  for (int64_t tile = xcd + 8 * slot; tile < n_tiles; tile += 8 * kBulkSlots) {
+    const int64_t tile0 = tile * kBulkTile + 64 * w;
+    Dest dst[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) dst[nt] = resolve(a, tile0 + nt * 16 + n);
 
-  if (a.latent_rot != nullptr) {
-    // Already rotated: load z straight into the accumulator layout.
+    f4 acc[4][8];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t tok = tile0 + nt * 16 + n;
-      if (tok < a.n_tokens) {
-        const float *src = a.latent_rot + tok * RLQ_DC + G * RLQ_GROUP + 4 * kg;
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = *(const f4 *)(src + 16 * mt);
+      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+
+    if (a.latent_rot != nullptr) {
+      // Already rotated: load z straight into the accumulator layout.
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int64_t tok = tile0 + nt * 16 + n;
+        if (tok < a.n_tokens) {
+          const float *src = a.latent_rot + tok * RLQ_DC + G * RLQ_GROUP + 4 * kg;
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = *(const f4 *)(src + 16 * mt);
+        }
       }
-    }
-  } else {
-    const uint16_t *rrow = a.rotation + (size_t)(G * RLQ_GROUP + n) * RLQ_DC + 8 * kg;
-    const uint16_t *crow[4];
-    bool cval[4];
+    } else {
+      // Latents of this wave's tokens; tokens past the end read the last
+      // token (their results are never stored).
+      const uint16_t *crow[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t tok = tile0 + nt * 16 + n;
-      cval[nt] = tok < a.n_tokens;
-      crow[nt] = a.latent + (cval[nt] ? tok : 0) * RLQ_DC + 8 * kg;
-    }
-    u4 ra[8], cb[4];
+      for (int nt = 0; nt < 4; ++nt) {
+        const int64_t tok = tile0 + nt * 16 + n;
+        crow[nt] = a.latent + (tok < a.n_tokens ? tok : a.n_tokens - 1) * RLQ_DC + 8 * kg;
+      }
+      // Latent K-slices run kCDepth steps ahead; the loop is fully unrolled so
+      // every buffer index is a constant.
+      constexpr int kSteps = RLQ_DC / 32;
+      constexpr int kCDepth = 3;
+      u4 cb[kCDepth][4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ra[mt] = *(const u4 *)(rrow + (size_t)16 * mt * RLQ_DC);
+      for (int k = 0; k < kCDepth; ++k)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) cb[nt] = cval[nt] ? *(const u4 *)crow[nt] : u4{0, 0, 0, 0};
-    for (int k = 0; k < RLQ_DC / 32; ++k) {
-      u4 ra_n[8], cb_n[4];
-      if (k + 1 < RLQ_DC / 32) {
+        for (int nt = 0; nt < 4; ++nt) cb[k][nt] = *(const u4 *)(crow[nt] + 32 * k);
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) {
+        u4 c[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) c[nt] = cb[k % kCDepth][nt];
+        if (k + kCDepth < kSteps) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) cb[k % kCDepth][nt] = *(const u4 *)(crow[nt] + 32 * (k + kCDepth));
+        }
+        // All eight A operands of the step are read up front, so one LDS
+        // wait covers them.
+        u4 ra[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) ra[mt] = *(const u4 *)(rs + chunk(k, 16 * mt + n, kg));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-          ra_n[mt] = *(const u4 *)(rrow + (size_t)16 * mt * RLQ_DC + 32 * (k + 1));
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          cb_n[nt] = cval[nt] ? *(const u4 *)(crow[nt] + 32 * (k + 1)) : u4{0, 0, 0, 0};
+          for (int nt = 0; nt < 4; ++nt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, ra[mt]), __builtin_bit_cast(bf16x8, c[nt]), acc[nt][mt], 0, 0, 0);
       }
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float z[8][4];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, ra[mt]), __builtin_bit_cast(bf16x8, cb[nt]),
-              acc[nt][mt], 0, 0, 0);
-      if (k + 1 < RLQ_DC / 32) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) ra[mt] = ra_n[mt];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) cb[nt] = cb_n[nt];
-      }
+        for (int i = 0; i < 4; ++i) z[mt][i] = acc[nt][mt][i];
+      finish_group(a, z, tile0 + nt * 16 + n, dst[nt], G, kg);
     }
+    // RoPE keys: group-0 workgroups, lane group kg copies N-tile kg.
+    if (G == 0) copy_rope_token(a, tile0 + kg * 16 + n, dst[kg]);
   }
-
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    float z[8][4];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[mt][i] = acc[nt][mt][i];
-    finish_group(a, z, tile0 + nt * 16 + n, G, kg);
-  }
-
-  copy_rope(a, tile0, kAppTokens, threadIdx.x, 256);
 }
 
 
@@ -234,6 +294,7 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   const int64_t tile0 = (int64_t)blockIdx.x * 16;
   const int64_t tok = tile0 + n;
   const bool cval = tok < a.n_tokens;
+  const Dest dst = resolve(a, tok);
   f4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -275,9 +336,9 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[mt][i] = v[i];
     }
-    finish_group(a, z, tok, G, kg);
+    finish_group(a, z, tok, dst, G, kg);
   }
-  if (G == 0) copy_rope(a, tile0, 16, threadIdx.x, 256);
+  if (G == 0 && w == 1 && kg == 0) copy_rope_token(a, tok, dst);
 }
 
 }  // namespace
@@ -288,8 +349,14 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
     const int64_t blocks = (a.n_tokens + 15) / 16;
     hipLaunchKernelGGL(append_small_kernel, dim3((unsigned)blocks, RLQ_NGROUPS), dim3(256), 0, stream, a);
   } else {
-    const int64_t blocks = (a.n_tokens + kAppTokens - 1) / kAppTokens;
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)append_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRBytes);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(append_kernel, dim3(kBulkGrid), dim3(64 * kBulkWaves), kRBytes, stream, a);
   }
   return hipGetLastError();
 }

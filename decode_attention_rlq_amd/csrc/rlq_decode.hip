@@ -167,32 +167,38 @@ __device__ inline u4 convert8(const u4 &w0, const u4 &w1, int h) {
   return r;
 }
 
-// What one lane loads for its token of one 16-token sub-tile, for the latent
-// half h of its wave (K-steps 8h .. 8h+7 and RoPE K-step h).
-struct SubLoad {
-  u4 cw;          // code words [4 q0 + 8h, 4 q0 + 8h + 4)
-  float mu, sd;   // (mean, scale) of group 2*(g>>1) + h
-  u4 rp;          // RoPE key elements [16g + 8h, 16g + 8h + 8)
-};
-// A wave tile: 32 consecutive tokens as two 16-token sub-tiles.
+// What one lane loads for its tokens of a wave tile (32 consecutive tokens as
+// two 16-token sub-tiles), for the latent half h of its wave (K-steps 8h ..
+// 8h+7 and RoPE K-step h).  Code words and RoPE key:
 struct TileLoad {
-  SubLoad s[2];
+  u4 cw[2];   // code words [4 q0 + 8h, 4 q0 + 8h + 4) of sub-tile 0 / 1
+  u4 rp[2];   // RoPE key elements [16g + 8h, 16g + 8h + 8)
 };
-
-__device__ inline void load_sub(const DecodeArgs &A, int64_t slot, int g4, int h, SubLoad &L) {
-  const int q0 = 4 * (g4 >> 1) + (g4 & 1);
-  L.cw = *(const u4 *)(A.codes + slot * RLQ_WORDS + 4 * q0 + 8 * h);
-  const float *m = A.meta + slot * 8 + 2 * (g4 >> 1) + h;
-  L.mu = m[0];
-  L.sd = m[4];
-  L.rp = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
-}
+// (mean, scale) of group 2*(g>>1) + h; fetched a tile earlier than the rest
+// since the decode tables need them first.
+struct MetaLoad {
+  float mu[2], sd[2];
+};
 
 // `first` = cache slot (page * 64 + 0 or 32) of the tile's first token.
 __device__ inline void load_tile(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
                                  TileLoad &L) {
-  load_sub(A, first + r16, g4, h, L.s[0]);
-  load_sub(A, first + 16 + r16, g4, h, L.s[1]);
+  const int q0 = 4 * (g4 >> 1) + (g4 & 1);
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int64_t slot = first + 16 * st + r16;
+    L.cw[st] = *(const u4 *)(A.codes + slot * RLQ_WORDS + 4 * q0 + 8 * h);
+    L.rp[st] = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
+  }
+}
+__device__ inline void load_meta(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
+                                 MetaLoad &L) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const float *m = A.meta + (first + 16 * st + r16) * 8 + 2 * (g4 >> 1) + h;
+    L.mu[st] = m[0];
+    L.sd[st] = m[4];
+  }
 }
 
 struct Protect {
@@ -275,8 +281,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   // The first two tiles' loads go out before the query staging, so their
   // latency overlaps it.
   TileLoad b0, b1;
+  MetaLoad m0, m1;
   if (!kProt && n_iter > 0) {
+    load_meta(A, tile_slot(0), r16, g4, h, m0);
     load_tile(A, tile_slot(0), r16, g4, h, b0);
+    load_meta(A, tile_slot(1), r16, g4, h, m1);
     load_tile(A, tile_slot(1), r16, g4, h, b1);
   }
 
@@ -344,27 +353,45 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   // than kLazy (log2 units), so O is rescaled rarely; P = 2^(s - m + kBias)
   // stays below 2^15.
   auto softmax = [&](const f4 &o0, const f4 &o1, int c0, int vlo, int vhi) {
-    // Full scores = own partial + partner's partial (the same sum, in the
+    // Full raw scores = own partial + partner's partial (the same sum, in the
     // same order, on both waves of the pair).
     f4 sc[2];
     sc[0] = h == 0 ? acc_prev[0] + o0 : o0 + acc_prev[0];
     sc[1] = h == 0 ? acc_prev[1] + o1 : o1 + acc_prev[1];
-    // sc[st][j] = score of token c0 + 16*st + 4*g4 + j, head r16.
-    if (c0 >= vlo && c0 + kWaveTok <= vhi) {
-      sc[0] *= A.scale_log2;
-      sc[1] *= A.scale_log2;
-    } else {
+    // sc[st][j] = raw score of token c0 + 16*st + 4*g4 + j, head r16.
+    if (!(c0 >= vlo && c0 + kWaveTok <= vhi)) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = c0 + 16 * st + 4 * g4 + j;
-          sc[st][j] = (t >= vlo && t < vhi) ? sc[st][j] * A.scale_log2 : kNegInf;
+          sc[st][j] = (t >= vlo && t < vhi) ? sc[st][j] : kNegInf;
         }
     }
+    half2v ph[4];
+    auto exps = [&]() {
+      // While no finite score has been seen the clamp keeps the exponent
+      // finite (exp2(-inf) = 0, never NaN).
+      const float mb = fmaxf(m_run, -1e30f) - kBias;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        ph[2 * st] = __builtin_convertvector(
+            (float2v){__builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][0], A.scale_log2, -mb)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][1], A.scale_log2, -mb))},
+            half2v);
+        ph[2 * st + 1] = __builtin_convertvector(
+            (float2v){__builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][2], A.scale_log2, -mb)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][3], A.scale_log2, -mb))},
+            half2v);
+      }
+    };
+    // P against the current running max first: the common case keeps the max
+    // reduction off the critical path.  When the tile exceeds the running max
+    // by more than kLazy the max moves, O is rescaled and P recomputed.
+    exps();
     float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mt = max_over_groups(mt);
+    mt = max_over_groups(mt) * A.scale_log2;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -372,17 +399,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
 #pragma unroll
       for (int j = 0; j < 16; ++j) O[j] *= alpha;
       m_run = m_new;
-    }
-    // While no finite score has been seen the clamp keeps exp2(-inf - mb) at
-    // 0 instead of NaN.
-    const float mb = fmaxf(m_run, -1e30f) - kBias;
-    half2v ph[4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      ph[2 * st] = __builtin_convertvector(
-          (float2v){__builtin_amdgcn_exp2f(sc[st][0] - mb), __builtin_amdgcn_exp2f(sc[st][1] - mb)}, half2v);
-      ph[2 * st + 1] = __builtin_convertvector(
-          (float2v){__builtin_amdgcn_exp2f(sc[st][2] - mb), __builtin_amdgcn_exp2f(sc[st][3] - mb)}, half2v);
+      exps();
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2(ph[j], (half2v){1.0f16, 1.0f16}, l_run, false);
@@ -483,34 +500,37 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   if constexpr (!kProt) {
     const int vlo = u_lo, vhi = u_hi < t_end ? u_hi : t_end;
     auto c0_of = [&](int i) { return t_begin + kWaveTok * (tile0 + i); };
-    auto run = [&](auto value_c, const TileLoad &cur, int i) {
+    auto run = [&](auto value_c, const TileLoad &cur, MetaLoad &meta, int i) {
       const int c0 = c0_of(i);
       Lut lut[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int t = c0 + 16 * st + r16;
-        lut[st] = make_lut(cur.s[st].mu, cur.s[st].sd, A.gain, A.level_inner, A.level_outer,
+        lut[st] = make_lut(meta.mu[st], meta.sd[st], A.gain, A.level_inner, A.level_outer,
                            t >= vlo && t < vhi);
       }
+      // The tables are built: the meta buffer takes tile i+2.
+      load_meta(A, tile_slot(i + 2), r16, g4, h, meta);
       auto dec = [&](int kl, int st) -> u4 {
-        return decode8(cur.s[st].cw[(kl >> 1) & 3], kl & 1, lut[st]);
+        return decode8(cur.cw[st][(kl >> 1) & 3], kl & 1, lut[st]);
       };
-      const u4 rp[2] = {cur.s[0].rp, cur.s[1].rp};
+      const u4 rp[2] = {cur.rp[0], cur.rp[1]};
       step(bool_c<true>{}, value_c, dec, rp, i, c0_of(i - 1), vlo, vhi);
     };
     if (n_iter > 0) {
-      // Two load buffers used alternately: the loads of tile i+1 are in
-      // flight while tile i is processed.  Loads are issued unconditionally
+      // Two load buffers used alternately: the code words and RoPE keys of
+      // tile i+1 (and the statistics of tile i+2) are in flight while tile i
+      // is processed.  Loads are issued unconditionally
       // (past the end the last tile is loaded again, from L2) so the loop
       // body has one straight path and the wait counts cover only the buffer
       // being consumed.
-      run(bool_c<false>{}, b0, 0);
+      run(bool_c<false>{}, b0, m0, 0);
       for (int i = 1; i < n_iter; i += 2) {
         load_tile(A, tile_slot(i + 1), r16, g4, h, b0);
-        run(bool_c<true>{}, b1, i);
+        run(bool_c<true>{}, b1, m1, i);
         if (i + 1 >= n_iter) break;
         load_tile(A, tile_slot(i + 2), r16, g4, h, b1);
-        run(bool_c<true>{}, b0, i + 1);
+        run(bool_c<true>{}, b0, m0, i + 1);
       }
       step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, c0_of(n_iter - 1), vlo, vhi);
     }
