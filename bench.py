@@ -1,18 +1,25 @@
-"""Benchmark: one decode step of the 2-bit MLA cache at the serving shape.
+"""Benchmark of the 2-bit MLA cache hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: quantize-append of
-the new token of each request (rotate, standardize, threshold, pack, RoPE
-copy) followed by absorbed-MLA decode attention over the paged 2-bit cache
-(split-KV + merge).  Default workload: 4 requests x 262,144 context tokens,
-16 heads, latent 512 + RoPE 64, group 128 (DeepSeek-V2-Lite MLA shapes at the
+Default workload (v2lite_256k): one decode step at the serving shape, i.e.
+quantize-append of the new token of each request (rotate, standardize,
+threshold, pack, RoPE copy) followed by absorbed-MLA decode attention over the
+paged 2-bit cache (split-KV + merge); 4 requests x 262,144 context tokens, 16
+heads, latent 512 + RoPE 64, group 128 (DeepSeek-V2-Lite MLA shapes at the
 pages' 256K-input, 4-concurrent-request serving point).
 
-Prints one JSON line.  `value` is context tokens per second of the whole step
-with every input already resident in HBM; `roofline` reports the decode call
-against MI355X's 8 TB/s HBM; `cpu_baseline` times the CPU oracle on the same
-step.
+Other workloads (each prints its own line with its own metric):
+  --config v2lite_32k      the same step at 4 x 32,768 tokens (16 cache replicas)
+  --config ragged_protect  32 requests of log-uniform 1K..64K tokens, 128 heads,
+                           4 sink + 64 recent BF16 tokens per request (MFMA-bound)
+  --config append_bulk     bulk quantize-append of 4 x 65,536 new tokens
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.  For the decode workloads `value` is context tokens per
+second of the whole step with every input already resident in HBM; `roofline`
+reports the decode call against MI355X's 8 TB/s HBM (or 2.5 PFLOP/s fp16 MFMA
+for 128 heads); `cpu_baseline` times the CPU oracle on a bounded sample of the
+same work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -29,13 +36,18 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "2-bit MLA decode context tokens/s and HBM GB/s (% peak) at B=4, 256K ctx"
+DECODE_METRIC = "2-bit MLA decode context tokens/s and HBM GB/s (% peak) at B=4, 256K ctx"
+APPEND_METRIC = "2-bit MLA quantize-append tokens/s, HBM GB/s and MFMA TFLOP/s (% peak), 4 x 65,536 new tokens"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 / bf16
 BYTES_PER_TOKEN = 288          # 128 B codes + 32 B fp32 stats + 128 B bf16 RoPE key
 BYTES_PER_PROTECTED = 1152     # 1024 B bf16 latent + 128 B RoPE key
+APPEND_BYTES_PER_TOKEN = 1024 + 128 + 288   # latent + RoPE key read, cache record written
+APPEND_FLOP_PER_TOKEN = 2 * 512 * 512       # z = R c
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_v2lite_256k.json")
 KERNEL_SOURCES = ["decode_attention_rlq_amd/csrc/rlq_decode.hip",
                   "decode_attention_rlq_amd/csrc/rlq_internal.h"]
+DEFAULT_REPLICAS = {"v2lite_256k": 2, "v2lite_32k": 16, "ragged_protect": 3}
 
 
 def log(msg):
@@ -50,16 +62,27 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def protected_count(ctx_lens, n_sink, n_recent):
+    return sum(min(int(c), n_sink + n_recent) for c in ctx_lens)
+
+
 def algorithmic_decode_bytes(batch, heads, ctx_lens, n_sink=0, n_recent=0):
-    prot = sum(min(int(c), n_sink + n_recent) for c in ctx_lens)
+    prot = protected_count(ctx_lens, n_sink, n_recent)
     toks = int(sum(int(c) for c in ctx_lens))
     return ((toks - prot) * BYTES_PER_TOKEN + prot * BYTES_PER_PROTECTED
             + batch * heads * (512 + 64) * 2 + batch * heads * 512 * 4)
 
 
-def measured_traffic():
+def decode_flops(heads, ctx_lens):
+    # scores over 576 dims + value product over 512 dims, per head and token
+    return 2.0 * heads * (576 + 512) * float(sum(int(c) for c in ctx_lens))
+
+
+def measured_traffic(config):
     """Per-launch HBM bytes from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    were taken on the current kernel source and this workload."""
+    if config != "v2lite_256k":
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -70,33 +93,258 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(prob, new_idx):
-    """Time the oracle on the same decode step (append of the new tokens +
-    decode over the full contexts) on the host cores."""
-    import oracle
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    log("cpu baseline: oracle setup (quantize the whole cache)")
-    oc = oracle.new_cache(prob.num_pages)
-    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits, prob.cu_seqlens, prob.start_pos,
-                           prob.block_table, latent_bf16=prob.latent_bits,
-                           rotation_bf16=prob.rotation_bits)
+        return len(os.sched_getaffinity(0))
+
+
+def copy_peak_gbps(torch, mib=1024, reps=5):
+    """Device-to-device copy rate (bytes read + written per second): the
+    practical HBM peak the decode is also compared against."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    return 2.0 * n / min(ts) / 1e9
+
+
+def pct(x):
+    return {"median_us": float(np.median(x)) * 1e3, "p10_us": float(np.percentile(x, 10)) * 1e3,
+            "p90_us": float(np.percentile(x, 90)) * 1e3}
+
+
+def dev_of(torch):
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+    return dev
+
+
+# --------------------------------------------------------------------------- CPU oracle baselines
+
+def cpu_baseline_decode(prob, new_idx, sample_requests):
+    """The oracle on the same decode step (append of the new tokens + decode
+    over the full contexts) for `sample_requests` of the batch."""
+    import oracle
+    reqs = list(range(min(sample_requests, prob.batch)))
+    log(f"cpu baseline: oracle setup (quantize the cache of {len(reqs)} request(s))")
+    oc = oracle.new_cache(prob.num_pages, max_batch=prob.batch, n_sink=prob.n_sink, n_recent=prob.n_recent)
+    cu = prob.cu_seqlens
+    sel = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in reqs])
+    sub_cu = np.zeros(len(reqs) + 1, np.int32)
+    sub_cu[1:] = np.cumsum([cu[b + 1] - cu[b] for b in reqs])
+    bt = prob.block_table[reqs]
+    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[sel], sub_cu, np.zeros(len(reqs), np.int32), bt,
+                           latent_bf16=prob.latent_bits[sel], rotation_bf16=prob.rotation_bits)
+    ctx = prob.ctx_lens[reqs]
     log("cpu baseline: timed oracle step")
     t0 = time.perf_counter()
-    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[new_idx], np.arange(prob.batch + 1),
-                           prob.ctx_lens - 1, prob.block_table,
-                           latent_bf16=prob.latent_bits[new_idx], rotation_bf16=prob.rotation_bits)
-    oracle.decode(oc, prob.q_c_bits, prob.q_r_bits, prob.sm_scale, prob.block_table, prob.ctx_lens,
+    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[new_idx[reqs]], np.arange(len(reqs) + 1),
+                           ctx - 1, bt, latent_bf16=prob.latent_bits[new_idx[reqs]],
+                           rotation_bf16=prob.rotation_bits)
+    oracle.decode(oc, prob.q_c_bits[reqs], prob.q_r_bits[reqs], prob.sm_scale, bt, ctx,
                   prob.gain, prob.level_inner, prob.level_outer)
     dt = time.perf_counter() - t0
-    toks = int(prob.ctx_lens.sum())
-    return {"value": toks / dt, "unit": "context tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full step of the same workload ({prob.batch} x {int(prob.ctx_lens[0])} "
-                      f"context tokens: append {prob.batch} tokens + decode), fp64 numpy, "
-                      f"{dt:.2f} s"}
+    toks = int(ctx.sum())
+    return {"value": toks / dt, "unit": "context tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"one step (append + fp64 decode) for {len(reqs)} of {prob.batch} requests, "
+                      f"{toks} context tokens, {prob.heads} heads: {dt:.2f} s"}
+
+
+def cpu_baseline_append(prob, n_sample):
+    import oracle
+    n = min(n_sample, int(prob.cu_seqlens[-1]))
+    oc = oracle.new_cache(prob.num_pages)
+    cu = np.array([0, n], np.int32)
+    log(f"cpu baseline: timed oracle quantize-append of {n} tokens")
+    t0 = time.perf_counter()
+    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[:n], cu, np.zeros(1, np.int32), prob.block_table[:1],
+                           latent_bf16=prob.latent_bits[:n], rotation_bf16=prob.rotation_bits)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"quantize-append of the first {n} new tokens (fp64 rotation): {dt:.2f} s"}
+
+
+# --------------------------------------------------------------------------- decode step
+
+def bench_decode(args, torch, rlq, workloads):
+    dev = dev_of(torch)
+    log(f"generating workload {args.config}")
+    prob = workloads.make_problem(args.config)
+    B, H = prob.batch, prob.heads
+    ctx = prob.ctx_lens.astype(np.int32)
+    prot = prob.n_sink > 0 or prob.n_recent > 0
+    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+    latent, rot, k_rope = dev(prob.latent_bits), dev(prob.rotation_bits), dev(prob.k_rope_bits)
+    bt, ctx_d = dev(prob.block_table), dev(ctx)
+    replicas = args.replicas or DEFAULT_REPLICAS.get(args.config, 2)
+    caches = []
+    for r in range(replicas):
+        log(f"prefill replica {r}: quantize-append {prob.n_tokens} tokens")
+        c = rlq.PagedCache.allocate(prob.num_pages, max_batch=B, n_sink=prob.n_sink, n_recent=prob.n_recent)
+        rlq.quantize_append(p, c, k_rope, dev(prob.cu_seqlens), dev(prob.start_pos), bt, latent=latent, rotation=rot)
+        caches.append(c)
+    torch.cuda.synchronize()
+    del latent
+
+    # The step's new tokens: the last position of each request is re-appended
+    # (so the context length stays fixed from step to step).
+    new_idx = (prob.cu_seqlens[1:] - 1).astype(np.int64)
+    new_lat, new_kr = dev(prob.latent_bits[new_idx]), dev(prob.k_rope_bits[new_idx])
+    new_cu, new_start = dev(np.arange(B + 1, dtype=np.int32)), dev(ctx - 1)
+    q_c, q_r = dev(prob.q_c_bits), dev(prob.q_r_bits)
+    max_ctx = int(ctx.max())
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(rlq.decode_workspace_size(B, H, max_ctx), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i, timed):
+        c = caches[i % len(caches)]
+        rlq.quantize_append(p, c, new_kr, new_cu, new_start, bt, latent=new_lat, rotation=rot,
+                            n_tokens=B, stream=stream)
+        if timed:
+            ev_a[i].record(stream)
+        rlq.mla_decode(p, c, q_c, q_r, prob.sm_scale, bt, ctx_d, max_ctx, out=out, lse=lse,
+                       workspace=ws, stream=stream)
+        if timed:
+            ev_b[i].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    dec_avg = float(dec_ms.mean())
+    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
+        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})")
+    copy_gbps = copy_peak_gbps(torch)
+    log(f"device copy rate {copy_gbps:.0f} GB/s")
+
+    toks = int(ctx.sum())
+    alg_bytes = algorithmic_decode_bytes(B, H, ctx, prob.n_sink if prot else 0, prob.n_recent if prot else 0)
+    gbps = alg_bytes / (dec_avg * 1e-3) / 1e9
+    tflops = decode_flops(H, ctx) / (dec_avg * 1e-3) / 1e12
+    hbm = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
+           "kernel": "rlq_mla_decode (split-KV kernel + merge kernel)",
+           "algorithmic_bytes_per_launch": alg_bytes, "copy_peak_gbps": copy_gbps,
+           "frac_of_copy_peak": gbps / copy_gbps}
+    mfma = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+            "kernel": "rlq_mla_decode (split-KV kernel + merge kernel)",
+            "algorithmic_flop_per_launch": decode_flops(H, ctx)}
+    # 16 heads: 121 flop per byte, HBM-bound; 128 heads: 967 flop per byte, MFMA-bound.
+    roofline, other = (mfma, hbm) if H >= 64 else (hbm, mfma)
+    roofline = dict(roofline)
+    roofline["other_bound"] = {k: other[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    workload = (f"{args.config}: decode step, B={B}, {toks} context tokens "
+                f"({'ragged ' if len(set(ctx.tolist())) > 1 else ''}{int(ctx.min())}..{int(ctx.max())} per request), "
+                f"{H} heads, latent 512 + RoPE 64, 2-bit codes, group 128, page 64"
+                + (f", {prob.n_sink} sink + {prob.n_recent} recent BF16 tokens" if prot else ""))
+    res = {
+        "metric": DECODE_METRIC if args.config == "v2lite_256k" else
+        f"2-bit MLA decode context tokens/s ({args.config})",
+        "value": toks / (ms_step * 1e-3),
+        "unit": "context tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": workload, "batch": B, "context_tokens": toks, "heads": H,
+                   "cache_replicas": replicas, "tau": prob.tau, "gain": prob.gain},
+        "decode_us": dec_avg * 1e3, "decode_percentiles": pct(dec_ms),
+        "decode_hbm_gbps": gbps,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(prob, new_idx, args.cpu_sample_requests or
+                                                  (prob.batch if H <= 16 else 2))
+    return res
+
+
+# --------------------------------------------------------------------------- bulk append
+
+def bench_append(args, torch, rlq, workloads):
+    dev = dev_of(torch)
+    log(f"generating workload {args.config}")
+    prob = workloads.make_problem(args.config)
+    n = int(prob.cu_seqlens[-1])
+    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+    c = rlq.PagedCache.allocate(prob.num_pages, max_batch=prob.batch)
+    lat, rot, kr = dev(prob.latent_bits), dev(prob.rotation_bits), dev(prob.k_rope_bits)
+    cu, sp, bt = dev(prob.cu_seqlens), dev(prob.start_pos), dev(prob.block_table)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        rlq.quantize_append(p, c, kr, cu, sp, bt, latent=lat, rotation=rot, n_tokens=n, stream=stream)
+
+    log(f"warmup {args.warmup} calls")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} calls")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    calls = np.array([a.elapsed_time(b) for a, b in evs])
+    t = float(calls.mean()) * 1e-3
+    log(f"append avg {t * 1e6:.1f} us (p10 {np.percentile(calls, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(calls, 90) * 1e3:.1f})")
+    copy_gbps = copy_peak_gbps(torch)
+    tflops = n * APPEND_FLOP_PER_TOKEN / t / 1e12
+    gbps = n * APPEND_BYTES_PER_TOKEN / t / 1e9
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                "kernel": "rlq_quantize_append (bulk kernel)",
+                "algorithmic_flop_per_launch": n * APPEND_FLOP_PER_TOKEN,
+                "other_bound": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": gbps / HBM_PEAK_GBPS},
+                "algorithmic_bytes_per_launch": n * APPEND_BYTES_PER_TOKEN, "copy_peak_gbps": copy_gbps}
+    res = {
+        "metric": APPEND_METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: quantize-append of {prob.batch} x {n // prob.batch} new tokens "
+                               f"(bf16 latent 512 + RoPE 64, Haar rotation, 1% Student-t coordinates)",
+                   "batch": prob.batch, "new_tokens": n, "tau": prob.tau},
+        "append_us": t * 1e6, "append_percentiles": pct(calls),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_append(prob, args.cpu_sample_tokens)
+    return res
 
 
 def main():
@@ -104,10 +352,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="v2lite_256k")
-    ap.add_argument("--replicas", type=int, default=2,
+    ap.add_argument("--config", default="v2lite_256k",
+                    choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk"])
+    ap.add_argument("--replicas", type=int, default=0,
                     help="cache copies cycled per step so no step reads a cache the MALL still holds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -130,111 +381,10 @@ def main():
     from decode_attention_rlq_amd import rlq, workloads
 
     torch.cuda.set_device(0)
-    log(f"generating workload {args.config}")
-    prob = workloads.make_problem(args.config)
-    B, H = prob.batch, prob.heads
-    ctx = prob.ctx_lens.astype(np.int32)
-
-    def dev(x):
-        x = np.ascontiguousarray(x)
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(x).cuda()
-
-    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
-    latent = dev(prob.latent_bits)
-    rot = dev(prob.rotation_bits)
-    k_rope = dev(prob.k_rope_bits)
-    bt = dev(prob.block_table)
-    ctx_d = dev(ctx)
-    caches = []
-    for r in range(args.replicas):
-        log(f"prefill replica {r}: quantize-append {prob.n_tokens} tokens")
-        c = rlq.PagedCache.allocate(prob.num_pages, max_batch=B, n_sink=prob.n_sink, n_recent=prob.n_recent)
-        rlq.quantize_append(p, c, k_rope, dev(prob.cu_seqlens), dev(prob.start_pos), bt,
-                            latent=latent, rotation=rot)
-        caches.append(c)
-    torch.cuda.synchronize()
-    del latent
-
-    # The step's new tokens: the last position of each request is re-appended
-    # (so the context length stays fixed from step to step).
-    new_idx = (prob.cu_seqlens[1:] - 1).astype(np.int64)
-    new_lat = dev(prob.latent_bits[new_idx])
-    new_kr = dev(prob.k_rope_bits[new_idx])
-    new_cu = dev(np.arange(B + 1, dtype=np.int32))
-    new_start = dev(ctx - 1)
-    q_c, q_r = dev(prob.q_c_bits), dev(prob.q_r_bits)
-    max_ctx = int(ctx.max())
-    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(rlq.decode_workspace_size(B, H, max_ctx), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    n_ev = args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-
-    def step(i, timed):
-        c = caches[i % len(caches)]
-        rlq.quantize_append(p, c, new_kr, new_cu, new_start, bt, latent=new_lat, rotation=rot,
-                            n_tokens=B, stream=stream)
-        if timed:
-            ev_a[i].record(stream)
-        rlq.mla_decode(p, c, q_c, q_r, prob.sm_scale, bt, ctx_d, max_ctx, out=out, lse=lse,
-                       workspace=ws, stream=stream)
-        if timed:
-            ev_b[i].record(stream)
-
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, True)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-    dec_avg = float(dec_ms.mean())
-    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
-        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})")
-
-    toks = int(ctx.sum())
-    alg_bytes = algorithmic_decode_bytes(B, H, ctx, prob.n_sink, prob.n_recent)
-    achieved = alg_bytes / (dec_avg * 1e-3) / 1e9
-    traffic = measured_traffic()
-    res = {
-        "metric": METRIC,
-        "value": toks / (ms_step * 1e-3),
-        "unit": "context tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16",
-        "data": "synthetic",
-        "config": {"workload": f"{args.config}: decode step, B={B} x {int(ctx[0])} context tokens, "
-                               f"{H} heads, latent 512 + RoPE 64, 2-bit codes, group 128, page 64",
-                   "batch": B, "ctx_per_request": int(ctx[0]), "heads": H,
-                   "cache_replicas": args.replicas, "tau": prob.tau, "gain": prob.gain},
-        "decode_us": dec_avg * 1e3,
-        "decode_hbm_gbps": achieved,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "rlq_mla_decode (split-KV kernel + merge kernel)",
-                     "algorithmic_bytes_per_launch": alg_bytes},
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(prob, new_idx)
+    if args.config == "append_bulk":
+        res = bench_append(args, torch, rlq, workloads)
+    else:
+        res = bench_decode(args, torch, rlq, workloads)
     print(json.dumps(res), flush=True)
 
 

@@ -293,27 +293,32 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   const int kg = lane >> 4;
   const int64_t tile0 = (int64_t)blockIdx.x * 16;
   const int64_t tok = tile0 + n;
-  const bool cval = tok < a.n_tokens;
-  const Dest dst = resolve(a, tok);
+  // Tokens past the end read the last token (their results are never stored).
+  const int64_t tok_c = tok < a.n_tokens ? tok : a.n_tokens - 1;
   f4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  Dest dst;
   if (a.latent_rot != nullptr) {
-    if (w == 0 && cval) {
-      const float *src = a.latent_rot + tok * RLQ_DC + G * RLQ_GROUP + 4 * kg;
+    if (w == 0) {
+      const float *src = a.latent_rot + tok_c * RLQ_DC + G * RLQ_GROUP + 4 * kg;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] = *(const f4 *)(src + 16 * mt);
     }
+    dst = resolve(a, tok);
   } else {
+    // Every load of the rotation goes out first; the destination lookup (a
+    // chain of dependent loads) runs while they are in flight.
     const uint16_t *rrow = a.rotation + (size_t)(G * RLQ_GROUP + n) * RLQ_DC + 128 * w + 8 * kg;
-    const uint16_t *crow = a.latent + (cval ? tok : 0) * RLQ_DC + 128 * w + 8 * kg;
+    const uint16_t *crow = a.latent + tok_c * RLQ_DC + 128 * w + 8 * kg;
     u4 ra[4][8], cb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      cb[k] = cval ? *(const u4 *)(crow + 32 * k) : u4{0, 0, 0, 0};
+      cb[k] = *(const u4 *)(crow + 32 * k);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) ra[k][mt] = *(const u4 *)(rrow + (size_t)16 * mt * RLQ_DC + 32 * k);
     }
+    dst = resolve(a, tok);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
