@@ -121,9 +121,27 @@ def copy_peak_gbps(torch, mib=1024, reps=5):
     return 2.0 * n / min(ts) / 1e9
 
 
-def pct(x):
-    return {"median_us": float(np.median(x)) * 1e3, "p10_us": float(np.percentile(x, 10)) * 1e3,
-            "p90_us": float(np.percentile(x, 90)) * 1e3}
+def timed_loop(torch, stream, fn, n, chunks=1):
+    """fn(0) .. fn(n-1) on `stream` with HIP events only at chunk boundaries
+    (an event record idles the GPU for a few microseconds, so none goes
+    between calls).  Returns (mean ms per call, per-chunk means in ms)."""
+    k = max(1, min(chunks, n))
+    bounds = [round(j * n / k) for j in range(k + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for j in range(k):
+        for i in range(bounds[j], bounds[j + 1]):
+            fn(i)
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per_chunk = [evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(k)]
+    return evs[0].elapsed_time(evs[k]) / n, per_chunk
+
+
+def spread(chunk_ms):
+    return {"chunks": len(chunk_ms), "chunk_mean_min_us": min(chunk_ms) * 1e3,
+            "chunk_mean_max_us": max(chunk_ms) * 1e3}
 
 
 def dev_of(torch):
@@ -213,36 +231,31 @@ def bench_decode(args, torch, rlq, workloads):
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.zeros(rlq.decode_workspace_size(B, H, max_ctx), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def step(i, timed):
-        c = caches[i % len(caches)]
-        rlq.quantize_append(p, c, new_kr, new_cu, new_start, bt, latent=new_lat, rotation=rot,
-                            n_tokens=B, stream=stream)
-        if timed:
-            ev_a[i].record(stream)
-        rlq.mla_decode(p, c, q_c, q_r, prob.sm_scale, bt, ctx_d, max_ctx, out=out, lse=lse,
+    def append(i):
+        rlq.quantize_append(p, caches[i % len(caches)], new_kr, new_cu, new_start, bt, latent=new_lat,
+                            rotation=rot, n_tokens=B, stream=stream)
+
+    def decode(i):
+        rlq.mla_decode(p, caches[i % len(caches)], q_c, q_r, prob.sm_scale, bt, ctx_d, max_ctx, out=out, lse=lse,
                        workspace=ws, stream=stream)
-        if timed:
-            ev_b[i].record(stream)
+
+    def step(i):
+        append(i)
+        decode(i)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, True)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-    dec_avg = float(dec_ms.mean())
-    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
-        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})")
+    ms_step, _ = timed_loop(torch, stream, step, args.steps)
+    # The decode call alone over the same caches, for the roofline: the mean
+    # over args.steps back-to-back calls, events only every fifth of them.
+    log(f"timing {args.steps} decode calls")
+    dec_avg, dec_chunks = timed_loop(torch, stream, decode, args.steps, chunks=5)
+    log(f"step {ms_step * 1e3:.1f} us, decode call {dec_avg * 1e3:.1f} us "
+        f"(chunk means {min(dec_chunks) * 1e3:.1f} .. {max(dec_chunks) * 1e3:.1f})")
     copy_gbps = copy_peak_gbps(torch)
     log(f"device copy rate {copy_gbps:.0f} GB/s")
 
@@ -277,7 +290,7 @@ def bench_decode(args, torch, rlq, workloads):
         "data": "synthetic",
         "config": {"workload": workload, "batch": B, "context_tokens": toks, "heads": H,
                    "cache_replicas": replicas, "tau": prob.tau, "gain": prob.gain},
-        "decode_us": dec_avg * 1e3, "decode_percentiles": pct(dec_ms),
+        "decode_us": dec_avg * 1e3, "decode_spread": spread(dec_chunks),
         "decode_hbm_gbps": gbps,
         "roofline": roofline,
     }
@@ -308,20 +321,9 @@ def bench_append(args, torch, rlq, workloads):
         call()
     torch.cuda.synchronize()
     log(f"timing {args.steps} calls")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for a, b in evs:
-        a.record(stream)
-        call()
-        b.record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    calls = np.array([a.elapsed_time(b) for a, b in evs])
-    t = float(calls.mean()) * 1e-3
-    log(f"append avg {t * 1e6:.1f} us (p10 {np.percentile(calls, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(calls, 90) * 1e3:.1f})")
+    ms, chunks = timed_loop(torch, stream, lambda i: call(), args.steps, chunks=5)
+    t = ms * 1e-3
+    log(f"append avg {t * 1e6:.1f} us (chunk means {min(chunks) * 1e3:.1f} .. {max(chunks) * 1e3:.1f})")
     copy_gbps = copy_peak_gbps(torch)
     tflops = n * APPEND_FLOP_PER_TOKEN / t / 1e12
     gbps = n * APPEND_BYTES_PER_TOKEN / t / 1e9
@@ -339,7 +341,7 @@ def bench_append(args, torch, rlq, workloads):
         "config": {"workload": f"{args.config}: quantize-append of {prob.batch} x {n // prob.batch} new tokens "
                                f"(bf16 latent 512 + RoPE 64, Haar rotation, 1% Student-t coordinates)",
                    "batch": prob.batch, "new_tokens": n, "tau": prob.tau},
-        "append_us": t * 1e6, "append_percentiles": pct(calls),
+        "append_us": t * 1e6, "append_spread": spread(chunks),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -74,20 +74,49 @@ __device__ inline float group_tree_sum(const float (&x)[8][4]) {
 }
 
 // Where a new token goes: its request, position and cache slot (-1 for
-// tokens past the end).  Resolved before the rotation so that the dependent
-// loads (request search, block table) overlap it.
+// tokens past the end), and the request's new length (read only when BF16
+// protection is on: the recent window is measured from it).
 struct Dest {
   int64_t slot;
   int32_t pos;  // position in the request (contexts stay below 2^31)
   int32_t b;
+  int32_t new_len;
 };
 
 __device__ inline Dest resolve(const AppendArgs &a, int64_t tok) {
-  Dest d{-1, 0, 0};
+  Dest d{-1, 0, 0, 0};
   if (tok >= a.n_tokens) return d;
   d.b = find_request(a.cu_seqlens, a.batch, tok);
-  d.pos = a.start_pos[d.b] + (int32_t)(tok - a.cu_seqlens[d.b]);
+  const int32_t start = a.start_pos[d.b], cu_b = a.cu_seqlens[d.b];
+  d.pos = start + (int32_t)(tok - cu_b);
   d.slot = (int64_t)a.block_table[(int64_t)d.b * a.max_pages + (d.pos >> 6)] * RLQ_PAGE + (d.pos & 63);
+  if (a.sink != nullptr || a.recent != nullptr) d.new_len = start + (a.cu_seqlens[d.b + 1] - cu_b);
+  return d;
+}
+
+// The same for the 16 tokens tile0 .. tile0+15, computed by one whole wave:
+// lane n < 16 gets token tile0 + n.  With fewer than 64 requests the request
+// search is one load of cu_seqlens (lane i holds cu_seqlens[i]) and 16
+// ballots, so the dependent chain is three loads long.
+__device__ inline Dest resolve_wave(const AppendArgs &a, int64_t tile0, int lane) {
+  if (a.batch >= 64) return resolve(a, tile0 + (lane & 15));
+  const int64_t tok = tile0 + (lane & 15);
+  const int32_t cu_l = a.cu_seqlens[lane <= a.batch ? lane : a.batch];
+  // Request of token t = number of i in [1, batch) with cu_seqlens[i] <= t.
+  int b = 0;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const uint64_t m =
+        __builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.batch && (int64_t)cu_l <= tile0 + n);
+    if ((lane & 15) == n) b = __builtin_popcountll(m);
+  }
+  const int32_t cu_b = __shfl(cu_l, b), cu_b1 = __shfl(cu_l, b + 1);
+  Dest d{-1, 0, b, 0};
+  if (tok >= a.n_tokens) return d;
+  const int32_t start = a.start_pos[b];
+  d.pos = start + (int32_t)(tok - cu_b);
+  d.slot = (int64_t)a.block_table[(int64_t)b * a.max_pages + (d.pos >> 6)] * RLQ_PAGE + (d.pos & 63);
+  d.new_len = start + (cu_b1 - cu_b);
   return d;
 }
 
@@ -147,7 +176,7 @@ __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4],
   }
   uint16_t *prot[2] = {nullptr, nullptr};
   if (a.sink == nullptr && a.recent == nullptr) return;
-  const int64_t new_len = (int64_t)a.start_pos[b] + (a.cu_seqlens[b + 1] - a.cu_seqlens[b]);
+  const int64_t new_len = dst_tok.new_len;
   if (a.sink != nullptr && pos < a.n_sink)
     prot[0] = a.sink + ((int64_t)b * a.n_sink + pos) * RLQ_DC;
   if (a.recent != nullptr && pos >= new_len - a.n_recent)
@@ -280,12 +309,17 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
 }
 
 
-// Few-token path (decode steps): workgroup (16-token tile, group G); wave w
-// contracts inputs [128w, 128w + 128) so every rotation load of the group is
-// in flight at once, then wave 0 adds the four partial products in a fixed
-// order and finishes the group.
-__global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
+// Few-token path (decode steps): workgroup (16-token tile, group G) of five
+// waves.  Wave w < 4 contracts inputs [128w, 128w + 128), so every rotation
+// load of the group is in flight at once; wave 4 looks up the destinations
+// (a chain of dependent loads that then waits behind no rotation load).
+// Wave 0 adds the four partial products in a fixed order and finishes the
+// group.
+constexpr int kSmallWaves = 5;
+
+__global__ __launch_bounds__(64 * kSmallWaves) void append_small_kernel(AppendArgs a) {
   __shared__ f4 part[4][8][64];
+  __shared__ Dest dests[16];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int G = blockIdx.y;
@@ -298,17 +332,16 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   f4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
-  Dest dst;
-  if (a.latent_rot != nullptr) {
+  if (w == 4) {
+    const Dest d = resolve_wave(a, tile0, lane);
+    if (lane < 16) dests[lane] = d;
+  } else if (a.latent_rot != nullptr) {
     if (w == 0) {
       const float *src = a.latent_rot + tok_c * RLQ_DC + G * RLQ_GROUP + 4 * kg;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] = *(const f4 *)(src + 16 * mt);
     }
-    dst = resolve(a, tok);
   } else {
-    // Every load of the rotation goes out first; the destination lookup (a
-    // chain of dependent loads) runs while they are in flight.
     const uint16_t *rrow = a.rotation + (size_t)(G * RLQ_GROUP + n) * RLQ_DC + 128 * w + 8 * kg;
     const uint16_t *crow = a.latent + tok_c * RLQ_DC + 128 * w + 8 * kg;
     u4 ra[4][8], cb[4];
@@ -318,15 +351,12 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) ra[k][mt] = *(const u4 *)(rrow + (size_t)16 * mt * RLQ_DC + 32 * k);
     }
-    dst = resolve(a, tok);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[k][mt]),
                                                           __builtin_bit_cast(bf16x8, cb[k]), acc[mt], 0, 0, 0);
-  }
-  if (a.latent_rot == nullptr) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) part[w][mt][lane] = acc[mt];
   }
@@ -341,9 +371,9 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[mt][i] = v[i];
     }
-    finish_group(a, z, tok, dst, G, kg);
+    finish_group(a, z, tok, dests[n], G, kg);
   }
-  if (G == 0 && w == 1 && kg == 0) copy_rope_token(a, tok, dst);
+  if (G == 0 && w == 1 && kg == 0) copy_rope_token(a, tok, dests[n]);
 }
 
 }  // namespace
@@ -352,7 +382,8 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
   if (a.n_tokens == 0) return hipSuccess;
   if (a.n_tokens <= kSmallTokens) {
     const int64_t blocks = (a.n_tokens + 15) / 16;
-    hipLaunchKernelGGL(append_small_kernel, dim3((unsigned)blocks, RLQ_NGROUPS), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(append_small_kernel, dim3((unsigned)blocks, RLQ_NGROUPS), dim3(64 * kSmallWaves), 0,
+                       stream, a);
   } else {
     static bool attr_set = false;
     if (!attr_set) {

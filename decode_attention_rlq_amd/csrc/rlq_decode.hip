@@ -53,8 +53,6 @@ constexpr int kPairs = kDecodeWaves / 2;           // wave pairs per workgroup
 constexpr int kChatBytes = kDecodeWaves * kWaveBytes;  // 128 KB
 constexpr int kXchBytes = kPairs * 2 * 2 * 2 * 64 * 16;  // [pair][parity][half][sub-tile] scores
 constexpr int kLdsBytes = kChatBytes + kXchBytes;      // 160 KB: one workgroup per CU
-constexpr int kQRow = RLQ_DC + 8;  // staged query row (halfs), padded against bank conflicts
-static_assert(16 * kQRow * 2 <= kChatBytes, "query staging fits");
 // Workgroups resident at once: one per CU x 256 CUs.
 constexpr int kResidentWorkgroups = 256;
 // Lazy online softmax: the running max m is raised only when a tile's max
@@ -169,36 +167,41 @@ __device__ inline u4 convert8(const u4 &w0, const u4 &w1, int h) {
 
 // What one lane loads for its tokens of a wave tile (32 consecutive tokens as
 // two 16-token sub-tiles), for the latent half h of its wave (K-steps 8h ..
-// 8h+7 and RoPE K-step h).  Code words and RoPE key:
-struct TileLoad {
-  u4 cw[2];   // code words [4 q0 + 8h, 4 q0 + 8h + 4) of sub-tile 0 / 1
-  u4 rp[2];   // RoPE key elements [16g + 8h, 16g + 8h + 8)
-};
-// (mean, scale) of group 2*(g>>1) + h; fetched a tile earlier than the rest
-// since the decode tables need them first.
-struct MetaLoad {
+// 8h+7 and RoPE K-step h).  Code words with the (mean, scale) of their group
+// 2*(g>>1) + h, fetched two tiles ahead; the RoPE key, needed only at the
+// end of a tile, is fetched as the tile starts.
+struct CodeLoad {
+  u4 cw[2];          // code words [4 q0 + 8h, 4 q0 + 8h + 4) of sub-tile 0 / 1
   float mu[2], sd[2];
 };
+struct RopeLoad {
+  u4 rp[2];          // RoPE key elements [16g + 8h, 16g + 8h + 8)
+};
 
-// `first` = cache slot (page * 64 + 0 or 32) of the tile's first token.
-__device__ inline void load_tile(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
-                                 TileLoad &L) {
-  const int q0 = 4 * (g4 >> 1) + (g4 & 1);
+// `first` = cache slot (page * 64 + 0 or 32) of the tile's first token, the
+// same for the whole wave: the row bases are scalar and the per-lane parts
+// 32-bit offsets.
+__device__ inline void load_codes(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
+                                  CodeLoad &L) {
+  const uint32_t q0 = 4 * (g4 >> 1) + (g4 & 1);
+  const uint32_t *cw = A.codes + first * RLQ_WORDS;
+  const float *mt = A.meta + first * 8;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+    L.cw[st] = *(const u4 *)(cw + (uint32_t)((16 * st + r16) * RLQ_WORDS + 4 * q0 + 8 * h));
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const int64_t slot = first + 16 * st + r16;
-    L.cw[st] = *(const u4 *)(A.codes + slot * RLQ_WORDS + 4 * q0 + 8 * h);
-    L.rp[st] = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
+    const uint32_t m = (16 * st + r16) * 8 + 2 * (g4 >> 1) + h;
+    L.mu[st] = mt[m];
+    L.sd[st] = mt[m + 4];
   }
 }
-__device__ inline void load_meta(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
-                                 MetaLoad &L) {
+__device__ inline void load_rope(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
+                                 RopeLoad &L) {
+  const uint16_t *rp = A.rope + first * RLQ_DR;
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const float *m = A.meta + (first + 16 * st + r16) * 8 + 2 * (g4 >> 1) + h;
-    L.mu[st] = m[0];
-    L.sd[st] = m[4];
-  }
+  for (int st = 0; st < 2; ++st)
+    L.rp[st] = *(const u4 *)(rp + (uint32_t)((16 * st + r16) * RLQ_DR + 16 * g4 + 8 * h));
 }
 
 struct Protect {
@@ -236,6 +239,17 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int HG = A.heads >> 4;
+  // The absorbed query (converted and staged below) is loaded first: it
+  // depends on nothing, and the page-id and code loads then overlap it.
+  constexpr int kQChunks = 16 * RLQ_DC / 8 / kDecodeThreads;  // 16-byte chunks per thread
+  u4 qv[kQChunks];
+  {
+    const uint16_t *qsrc = A.q_c + ((int64_t)b * A.heads + hg * 16) * RLQ_DC;
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) qv[j] = *(const u4 *)(qsrc + 8 * (threadIdx.x + j * kDecodeThreads));
+  }
+  const bf16x8 qrB = __builtin_bit_cast(
+      bf16x8, *(const u4 *)(A.q_r + ((int64_t)b * A.heads + hg * 16 + r16) * RLQ_DR + 16 * g4 + 8 * h));
   const int ctx = A.ctx_lens[b];
   const Protect pr_ = protect_range(A, ctx);
   // Token range of this workgroup: positions for ordinary splits, indices
@@ -251,63 +265,65 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   }
   const int u_lo = pr_.ns, u_hi = ctx - pr_.nr;  // unprotected positions
 
-  // Tiles of the workgroup; every pair runs the same number of iterations,
-  // tiles past the range are fully masked.
+  // Tiles of the workgroup.  An ordinary split deals its nominal tile count
+  // (tokens_per_split / 32) out to the pairs, so each pair's page ids can be
+  // fetched before the context length is known; in a split cut short by the
+  // context the last pairs get fewer tiles or none.  The protected workgroup
+  // deals its tiles evenly (every pair runs n_iter steps, tiles past the end
+  // masked).
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + kWaveTok - 1) / kWaveTok : 0;
-  const int n_iter = (n_tiles + kPairs - 1) / kPairs;
+  const int n_iter = kProt ? (n_tiles + kPairs - 1) / kPairs
+                           : (A.tokens_per_split / kWaveTok + kPairs - 1) / kPairs;
   const int tile0 = pr * n_iter;
-  // Page ids of the workgroup's range in VGPRs (lane l of register c holds
-  // page p_first + 64c + l): a tile's loads need no memory access for them.
+  const int n_mine = min(max(n_tiles - tile0, 0), n_iter);  // ordinary splits: tiles of this pair
+  // Page ids of the pair's tiles in one VGPR: lane l holds page
+  // p_first + (tile0 >> 1) + l (a pair's tiles span at most 64 pages), so a
+  // tile's loads need one readlane and no memory access for their page.
   const int p_first = t_begin >> 6;
-  const int n_pages = kProt ? 0 : (n_tiles + 1) >> 1;
-  int32_t pid_v[kMaxSplitPages / 64];
-#pragma unroll
-  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
-    const int i = 64 * c + lane;
-    pid_v[c] = i < n_pages ? A.block_table[(int64_t)b * A.max_pages + p_first + i] : 0;
-  }
-  auto page_id = [&](int i) -> int32_t {  // i wave-uniform, < n_pages
-    int32_t v = __builtin_amdgcn_readlane(pid_v[0], i & 63);
-#pragma unroll
-    for (int c = 1; c < kMaxSplitPages / 64; ++c)
-      if ((i >> 6) == c) v = __builtin_amdgcn_readlane(pid_v[c], i & 63);
-    return v;
-  };
-  const int last = n_tiles - 1;
+  const int pp0 = tile0 >> 1;
+  const int32_t pid_pair = (!kProt && p_first + pp0 + lane < A.max_pages)
+                               ? A.block_table[(int64_t)b * A.max_pages + p_first + pp0 + lane]
+                               : 0;
+  const int last_mine = tile0 + n_mine - 1;
   auto tile_slot = [&](int i) -> int64_t {  // i = pair-local tile index
-    const int c = t_begin + kWaveTok * min(tile0 + i, last);
-    return (int64_t)page_id((c >> 6) - p_first) * RLQ_PAGE + (c & 63);
+    // Past the pair's last tile the last one is loaded again (never
+    // consumed); a pair without tiles loads cache slot 0 (never consumed).
+    const int t = min(tile0 + i, last_mine);
+    const int64_t s = (int64_t)__builtin_amdgcn_readlane(pid_pair, (t >> 1) - pp0) * RLQ_PAGE +
+                      ((t_begin + kWaveTok * t) & 63);
+    return n_mine > 0 ? s : 0;
   };
-  // The first two tiles' loads go out before the query staging, so their
-  // latency overlaps it.
-  TileLoad b0, b1;
-  MetaLoad m0, m1;
-  if (!kProt && n_iter > 0) {
-    load_meta(A, tile_slot(0), r16, g4, h, m0);
-    load_tile(A, tile_slot(0), r16, g4, h, b0);
-    load_meta(A, tile_slot(1), r16, g4, h, m1);
-    load_tile(A, tile_slot(1), r16, g4, h, b1);
+  // ---- absorbed query of 16 heads, converted to fp16 and scattered through
+  // LDS into operand order: row (head) hd, K-step k, lane group g, slot j at
+  // qslot(hd, k, g) + 2j.  The first two tiles' code loads go out before
+  // it, so their latency overlaps the staging.
+  constexpr int kQHead = 16 * 4 * 16 + 16;  // bytes per head row, padded against bank conflicts
+  static_assert(16 * kQHead <= kChatBytes, "query staging fits");
+  auto qslot = [](int hd, int k, int g) { return hd * kQHead + (k * 4 + g) * 16; };
+  CodeLoad c0, c1, c2;
+  if constexpr (!kProt) {
+    load_codes(A, tile_slot(0), r16, g4, h, c0);
+    load_codes(A, tile_slot(1), r16, g4, h, c1);
   }
-
-  // ---- absorbed query of 16 heads, staged through LDS into operand order;
-  // wave h keeps K-steps 8h .. 8h+7 and RoPE K-step h.
-  {
-    const uint16_t *qsrc = A.q_c + ((int64_t)b * A.heads + hg * 16) * RLQ_DC;
-    for (int c = threadIdx.x; c < 16 * RLQ_DC / 8; c += kDecodeThreads)
-      *(u4 *)(smem + 2 * kQRow * (c >> 6) + 16 * (c & 63)) = *(const u4 *)(qsrc + 8 * c);
+#pragma unroll
+  for (int j = 0; j < kQChunks; ++j) {
+    const int c = threadIdx.x + j * kDecodeThreads;
+    const int hd = c >> 6;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // Latent coordinate x = 16 word + sub, inverted through coord_of.
+      const int x = 8 * (c & 63) + e, word = x >> 4, sub = x & 15, w2 = word >> 2;
+      const int k = 8 * ((w2 >> 1) & 1) + 2 * (word & 3) + ((sub >> 1) & 1);
+      const int g = ((w2 >> 2) << 1) | (w2 & 1);
+      const int jj = 4 * (sub & 1) + (sub >> 2);
+      const uint32_t v = (e & 1) ? (qv[j][e >> 1] >> 16) : (qv[j][e >> 1] & 0xFFFFu);
+      *(_Float16 *)(smem + qslot(hd, k, g) + 2 * jj) = (_Float16)bf16_to_f32(v);
+    }
   }
   __syncthreads();
   half8 qB[8];
-  {
-    const uint16_t *qs = (const uint16_t *)smem + r16 * kQRow;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        qB[k][j] = (_Float16)bf16_to_f32(qs[coord_of(8 * h + k, g4, j)]);
-  }
-  const bf16x8 qrB = __builtin_bit_cast(
-      bf16x8, *(const u4 *)(A.q_r + ((int64_t)b * A.heads + hg * 16 + r16) * RLQ_DR + 16 * g4 + 8 * h));
+  for (int k = 0; k < 8; ++k) qB[k] = *(const half8 *)(smem + qslot(r16, 8 * h + k, g4));
   // Exchange slots of partial scores, [pair][parity][half][sub-tile][64 lanes].
   // A slot holding kPoison in any element is empty: the reader re-poisons a
   // slot after consuming it, so readiness needs no flag and no barrier.
@@ -334,18 +350,17 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   const int vrd = 1024 * va + 16 * ((4 * g4 + (r16 >> 2)) ^ (8 * va)) + 8 * (r16 & 1);
 
   // Tile pipeline.  Step i (pair-local tile index) runs, in program order:
-  //   part 1  - transposed reads of tile i-1's K-step pair 0 into registers,
-  //             decode + partial scores of tile i's K-step pair 0 (its c_hat
-  //             overwrites those slots: LDS operations of a wave run in order);
-  //   softmax - barrier, the partner's partial scores of tile i-1, online
-  //             softmax of tile i-1 -> P;
+  //   part 1  - own partial scores of tile i-1 (finished in step i-1) out to
+  //             the exchange slots and the partner's read back; transposed
+  //             reads of tile i-1's K-step pair 0; decode + partial scores of
+  //             tile i's K-step pair 0 (its c_hat overwrites those slots: LDS
+  //             operations of a wave run in order);
+  //   softmax - the partner's partial of tile i-1 (polled if not there yet),
+  //             online softmax of tile i-1 -> P;
   //   part 2  - value product O^T += c_hat^T P^T of tile i-1 (pair 0 from
   //             registers, pairs 1..3 read just before tile i overwrites
   //             them), decode + partial scores of tile i's pairs 1..3, RoPE
-  //             part, own partial scores of tile i to the exchange buffer.
-  // The partner's partial of tile i-1 was written a whole step earlier, so the
-  // barrier rarely waits, and the exponentials share a basic block with the
-  // decode of tile i.
+  //             part, decode tables of tile i+1.
   f4 acc_prev[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 
   // Online softmax of the pair's tile i (partial scores of this wave in
@@ -431,9 +446,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   };
 
   // kScore: tile i is new (decode + partial scores); kValue: tile i-1 gets its
-  // softmax and value product.
+  // softmax and value product.  `tail` runs once the step's last code word is
+  // decoded (the next tile's tables are built there).
   auto step = [&](auto score_c, auto value_c, auto &&dec, const u4 (&rp)[2], int i, int c0_prev,
-                  int vlo, int vhi) {
+                  int vlo, int vhi, auto &&tail) {
     constexpr bool kScore = decltype(score_c)::value;
     constexpr bool kValue = decltype(value_c)::value;
     f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
@@ -451,9 +467,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
     f4 o0, o1;
     f4 *other = xch_at(i - 1, h ^ 1);
     if constexpr (kValue) {
-      // The partner's partial of tile i-1 (written at the end of its
-      // previous step); the read is issued before part 1 so that waiting for
-      // it does not wait for part 1's LDS traffic.
+      // This wave's partial of tile i-1, finished in the previous step, is
+      // published now rather than at the end of that step, so no wave waits
+      // there for its last MFMAs.  The partner does the same; its partial is
+      // read here and consumed after part 1.
+      f4 *mine = xch_at(i - 1, h);
+      mine[lane] = acc_prev[0];
+      mine[64 + lane] = acc_prev[1];
       o0 = other[lane];
       o1 = other[64 + lane];
       tr_pair(0, av0);
@@ -487,52 +507,56 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
-      f4 *mine = xch_at(i, h);
-      mine[lane] = acc[0];
-      mine[64 + lane] = acc[1];
+      tail();
       acc_prev[0] = acc[0];
       acc_prev[1] = acc[1];
     }
   };
   auto no_dec = [](int, int) -> u4 { return u4{0, 0, 0, 0}; };
+  auto no_tail = []() {};
   const u4 no_rp[2] = {};
 
   if constexpr (!kProt) {
     const int vlo = u_lo, vhi = u_hi < t_end ? u_hi : t_end;
     auto c0_of = [&](int i) { return t_begin + kWaveTok * (tile0 + i); };
-    auto run = [&](auto value_c, const TileLoad &cur, MetaLoad &meta, int i) {
-      const int c0 = c0_of(i);
-      Lut lut[2];
+    // Decode tables of the tile being decoded; the tail of each step replaces
+    // them with the next tile's.
+    Lut lut[2];
+    auto build_lut = [&](const CodeLoad &L, int i) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int t = c0 + 16 * st + r16;
-        lut[st] = make_lut(meta.mu[st], meta.sd[st], A.gain, A.level_inner, A.level_outer,
-                           t >= vlo && t < vhi);
+        const int t = c0_of(i) + 16 * st + r16;
+        lut[st] = make_lut(L.mu[st], L.sd[st], A.gain, A.level_inner, A.level_outer, t >= vlo && t < vhi);
       }
-      // The tables are built: the meta buffer takes tile i+2.
-      load_meta(A, tile_slot(i + 2), r16, g4, h, meta);
+    };
+    RopeLoad rb;
+    // Step i: `cur` holds tile i's codes, `next` tile i+1's, `far` takes
+    // tile i+2's.  The RoPE load goes out before the far codes, so waiting
+    // for it at the end of the step does not wait for them.
+    auto run = [&](auto value_c, const CodeLoad &cur, const CodeLoad &next, CodeLoad &far, int i) {
+      load_rope(A, tile_slot(i), r16, g4, h, rb);
+      load_codes(A, tile_slot(i + 2), r16, g4, h, far);
       auto dec = [&](int kl, int st) -> u4 {
         return decode8(cur.cw[st][(kl >> 1) & 3], kl & 1, lut[st]);
       };
-      const u4 rp[2] = {cur.rp[0], cur.rp[1]};
-      step(bool_c<true>{}, value_c, dec, rp, i, c0_of(i - 1), vlo, vhi);
+      auto tail = [&]() { build_lut(next, i + 1); };
+      step(bool_c<true>{}, value_c, dec, rb.rp, i, c0_of(i - 1), vlo, vhi, tail);
     };
-    if (n_iter > 0) {
-      // Two load buffers used alternately: the code words and RoPE keys of
-      // tile i+1 (and the statistics of tile i+2) are in flight while tile i
-      // is processed.  Loads are issued unconditionally
-      // (past the end the last tile is loaded again, from L2) so the loop
-      // body has one straight path and the wait counts cover only the buffer
-      // being consumed.
-      run(bool_c<false>{}, b0, m0, 0);
-      for (int i = 1; i < n_iter; i += 2) {
-        load_tile(A, tile_slot(i + 1), r16, g4, h, b0);
-        run(bool_c<true>{}, b1, m1, i);
-        if (i + 1 >= n_iter) break;
-        load_tile(A, tile_slot(i + 2), r16, g4, h, b1);
-        run(bool_c<true>{}, b0, m0, i + 1);
+    if (n_mine > 0) {
+      // Three code buffers used in turn: tile i+1's and tile i+2's codes are
+      // in flight while tile i is processed.  Loads are issued
+      // unconditionally (past the end the last tile is loaded again, from
+      // L2) so the loop body has one straight path.
+      build_lut(c0, 0);
+      run(bool_c<false>{}, c0, c1, c2, 0);
+      for (int i = 1; i < n_mine; i += 3) {
+        run(bool_c<true>{}, c1, c2, c0, i);
+        if (i + 1 >= n_mine) break;
+        run(bool_c<true>{}, c2, c0, c1, i + 1);
+        if (i + 2 >= n_mine) break;
+        run(bool_c<true>{}, c0, c1, c2, i + 2);
       }
-      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, c0_of(n_iter - 1), vlo, vhi);
+      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_mine, c0_of(n_mine - 1), vlo, vhi, no_tail);
     }
   } else {
     // Protected list index v -> position and BF16 source row.
@@ -561,12 +585,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
         return convert8(w0, w1, kl & 1);
       };
       if (i == 0)
-        step(bool_c<true>{}, bool_c<false>{}, dec, rp, i, 0, 0, t_end);
+        step(bool_c<true>{}, bool_c<false>{}, dec, rp, i, 0, 0, t_end, no_tail);
       else
-        step(bool_c<true>{}, bool_c<true>{}, dec, rp, i, c0 - kWaveTok, 0, t_end);
+        step(bool_c<true>{}, bool_c<true>{}, dec, rp, i, c0 - kWaveTok, 0, t_end, no_tail);
     }
     if (n_iter > 0)
-      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, kWaveTok * (tile0 + n_iter - 1), 0, t_end);
+      step(bool_c<false>{}, bool_c<true>{}, no_dec, no_rp, n_iter, kWaveTok * (tile0 + n_iter - 1), 0, t_end,
+           no_tail);
   }
 
   // ---- partial of the workgroup: pairs 1 .. kPairs-1 hand their (max, sum,
@@ -618,8 +643,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
 }
 
 // LSE merge of the per-split partials of one (request, head group) for one
-// value tile: 4 waves each sum a quarter of the splits with many loads in
-// flight, then the quarters are added in a fixed order.
+// value tile: 4 waves each sum a quarter of the splits, then the quarters are
+// added in a fixed order.  The first kMergePre partial tiles of every wave
+// are loaded before the statistics pass, so their latency overlaps it.
+constexpr int kMergePre = 16;
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
   __shared__ float wts[kMaxSplits + 1][16];
   __shared__ float red_m[16][16], red_l[16][16];
@@ -632,6 +660,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
   const float2 *ml = (const float2 *)(A.part_ml + (int64_t)bh * S * 32);
   const int tid = threadIdx.x;
   const int h = tid & 15, st = tid >> 4;
+  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
+  constexpr int kStride = kPartialFloats / 4;
+  const f4 *po = (const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats) + jp * 64 + lane;
+  // Wave grp takes splits grp, grp + 4, ...
+  f4 pre[kMergePre];
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u) {
+    const int s = grp + 4 * u;
+    pre[u] = s < S ? po[(int64_t)s * kStride] : f4{0.f, 0.f, 0.f, 0.f};
+  }
   // Max per head over the splits: thread (h, st) takes splits st, st+16, ...
   {
     float m = kNegInf;
@@ -655,11 +693,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
     red_l[st][h] = l;
   }
   __syncthreads();
-  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
-  const f4 *po = (const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats) + jp * 64 + lane;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kStride = kPartialFloats / 4;
-  int s = grp;
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u) {
+    const int s = grp + 4 * u;
+    if (s < S) acc += wts[s][hh] * pre[u];
+  }
+  int s = grp + 4 * kMergePre;
   for (; s + 28 < S; s += 32) {
     f4 v[8];
 #pragma unroll

@@ -50,6 +50,13 @@ CASES = {
                            n_sink=4, n_recent=16),
     "protect_4_64": dict(name="ragged_protect", ctx_lens=[70, 1, 300], start=[0, 0, 100],
                          heads=16, n_sink=4, n_recent=64),
+    # Requests with no new token between ones that have some (the request
+    # search must skip empty requests).
+    "empty_requests": dict(name="tiny", ctx_lens=[5, 9, 5, 70, 3], start=[5, 0, 5, 60, 3],
+                           n_sink=2, n_recent=4),
+    # 70 requests: more than one wave's worth of cu_seqlens entries.
+    "many_requests": dict(name="tiny", ctx_lens=[1 + (7 * b) % 11 for b in range(70)],
+                          start=[(3 * b) % 2 for b in range(70)], n_sink=1, n_recent=3),
 }
 
 
