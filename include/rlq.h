@@ -29,7 +29,8 @@
  *    call returns and never synchronizes: work is enqueued on `stream` and the
  *    caller keeps every buffer alive until the stream has completed it.  Its
  *    only process-wide state is a per-device "is gfx950" check result and the
- *    decode kernel's one-time LDS-size attribute, both set on first use.
+ *    one-time LDS-size attributes of the decode and bulk-append kernels, all set
+ *    on first use.
  *  - Device pointers must be 16-byte aligned and their arrays contiguous in
  *    the layouts given below.
  *  - Each call returns an RLQ_* status.  Host-side validation runs before any
