@@ -218,6 +218,91 @@ __device__ inline Protect protect_range(const DecodeArgs &A, int ctx) {
 template <bool V>
 using bool_c = std::integral_constant<bool, V>;
 
+// LSE merge of the per-split partials of one (request, head group) `bh` for
+// value tile `jp` (16 heads x 16 latent coordinates as 64 lanes x 4) by a
+// workgroup of four waves: wave w sums splits w, w + 4, ..., then the four
+// sums are added in a fixed order.  Each wave loads its first 16 partial tiles
+// before the statistics pass, so their latency overlaps it.
+constexpr int kMergeWaves = 4;
+constexpr int kMergePre = 16;
+
+__device__ void merge_tile(const DecodeArgs &A, int jp, int bh, float (*wts)[16], float (*red_m)[16],
+                           float (*red_l)[16], f4 (*part)[64]) {
+  const int HG = A.heads >> 4;
+  const int b = bh / HG, hg = bh % HG;
+  const int S = A.splits + A.prot;
+  const float2 *ml = (const float2 *)(A.part_ml + (int64_t)bh * S * 32);
+  const int tid = threadIdx.x;
+  const int h = tid & 15, st = tid >> 4;
+  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
+  constexpr int kStride = kPartialFloats / 4;
+  const f4 *po = (const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats) + jp * 64 + lane;
+  f4 pre[kMergePre];
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u) {
+    const int s = grp + kMergeWaves * u;
+    pre[u] = s < S ? po[(int64_t)s * kStride] : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    // Max per head over the splits: thread (h, st) takes splits st, st + 16, ...
+    float m = kNegInf;
+#pragma unroll 4
+    for (int s = st; s < S; s += 16) m = fmaxf(m, ml[s * 16 + h].x);
+    red_m[st][h] = m;
+  }
+  __syncthreads();
+  {
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, red_m[i][h]);
+    float l = 0.f;
+#pragma unroll 4
+    for (int s = st; s < S; s += 16) {
+      const float2 v = ml[s * 16 + h];
+      const float w = __builtin_amdgcn_exp2f(v.x - fmaxf(M, -1e30f));  // 0 for empty splits
+      wts[s][h] = w;
+      l += w * v.y;
+    }
+    red_l[st][h] = l;
+  }
+  __syncthreads();
+  {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+      const int s = grp + kMergeWaves * u;
+      if (s < S) acc += wts[s][hh] * pre[u];
+    }
+    int s = grp + kMergeWaves * kMergePre;
+    for (; s + 7 * kMergeWaves < S; s += 8 * kMergeWaves) {
+      f4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = po[(int64_t)(s + kMergeWaves * u) * kStride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wts[s + kMergeWaves * u][hh] * v[u];
+    }
+    for (; s < S; s += kMergeWaves) acc += wts[s][hh] * po[(int64_t)s * kStride];
+    part[grp][lane] = acc;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) L += red_l[i][hh];
+    float Mh = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
+    const f4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float *o = A.out + ((int64_t)b * A.heads + hg * 16 + hh) * RLQ_DC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
+    if (A.lse != nullptr && jp == 0 && lane < 16)
+      A.lse[(int64_t)b * A.heads + hg * 16 + lane] =
+          L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+  }
+}
+
 // kProt = false: the ordinary splits (partials prot .. prot + splits - 1 of a
 // request); kProt = true: the BF16 sink/recent tokens (partial 0).
 //
@@ -642,90 +727,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   }
 }
 
-// LSE merge of the per-split partials of one (request, head group) for one
-// value tile: 4 waves each sum a quarter of the splits, then the quarters are
-// added in a fixed order.  The first kMergePre partial tiles of every wave
-// are loaded before the statistics pass, so their latency overlaps it.
-constexpr int kMergePre = 16;
-
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
+// The standalone merge: 32 workgroups of 4 waves per (request, head group).
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs A) {
   __shared__ float wts[kMaxSplits + 1][16];
   __shared__ float red_m[16][16], red_l[16][16];
-  __shared__ f4 part[4][64];
-  const int jp = blockIdx.x;  // value tile 0..31
-  const int bh = blockIdx.y;  // b * HG + hg
-  const int HG = A.heads >> 4;
-  const int b = bh / HG, hg = bh % HG;
-  const int S = A.splits + A.prot;
-  const float2 *ml = (const float2 *)(A.part_ml + (int64_t)bh * S * 32);
-  const int tid = threadIdx.x;
-  const int h = tid & 15, st = tid >> 4;
-  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
-  constexpr int kStride = kPartialFloats / 4;
-  const f4 *po = (const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats) + jp * 64 + lane;
-  // Wave grp takes splits grp, grp + 4, ...
-  f4 pre[kMergePre];
-#pragma unroll
-  for (int u = 0; u < kMergePre; ++u) {
-    const int s = grp + 4 * u;
-    pre[u] = s < S ? po[(int64_t)s * kStride] : f4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Max per head over the splits: thread (h, st) takes splits st, st+16, ...
-  {
-    float m = kNegInf;
-#pragma unroll 4
-    for (int s = st; s < S; s += 16) m = fmaxf(m, ml[s * 16 + h].x);
-    red_m[st][h] = m;
-  }
-  __syncthreads();
-  float M = kNegInf;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) M = fmaxf(M, red_m[i][h]);
-  {
-    float l = 0.f;
-#pragma unroll 4
-    for (int s = st; s < S; s += 16) {
-      const float2 v = ml[s * 16 + h];
-      const float w = __builtin_amdgcn_exp2f(v.x - fmaxf(M, -1e30f));  // 0 for empty splits
-      wts[s][h] = w;
-      l += w * v.y;
-    }
-    red_l[st][h] = l;
-  }
-  __syncthreads();
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < kMergePre; ++u) {
-    const int s = grp + 4 * u;
-    if (s < S) acc += wts[s][hh] * pre[u];
-  }
-  int s = grp + 4 * kMergePre;
-  for (; s + 28 < S; s += 32) {
-    f4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = po[(int64_t)(s + 4 * u) * kStride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += wts[s + 4 * u][hh] * v[u];
-  }
-  for (; s < S; s += 4) acc += wts[s][hh] * po[(int64_t)s * kStride];
-  part[grp][lane] = acc;
-  __syncthreads();
-  if (grp == 0) {
-    float L = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) L += red_l[i][hh];
-    float Mh = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
-    const f4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float *o = A.out + ((int64_t)b * A.heads + hg * 16 + hh) * RLQ_DC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
-    if (A.lse != nullptr && jp == 0 && lane < 16)
-      A.lse[(int64_t)b * A.heads + hg * 16 + lane] =
-          L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
-  }
+  __shared__ f4 part[kMergeWaves][64];
+  merge_tile(A, blockIdx.x, blockIdx.y, wts, red_m, red_l, part);
 }
 
 }  // namespace
@@ -771,11 +778,11 @@ hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.splits, batch, hg), dim3(kDecodeThreads),
-                     kLdsBytes, stream, a);
+  const dim3 grid(a.splits, batch, hg);
+  hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(kDecodeThreads), kLdsBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(32, batch * hg), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(32, batch * hg), dim3(64 * kMergeWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,6 +26,9 @@ DECODE_CASES = {
     "protect_4_16": dict(name="ragged_protect", ctx_lens=[19, 20, 21, 700], heads=16, n_recent=16),
     "h128_protect": dict(name="ragged_protect", ctx_lens=[1500, 77], heads=128),
     "tau_gain_extremes": dict(name="v2lite_32k", ctx_lens=[300, 900], tau=0.85, gain=1.2),
+    # 34 requests x 8 head groups: more split workgroups than the GPU holds at
+    # once, so the merge runs as its own kernel.
+    "wide_batch_h128": dict(name="ragged_protect", ctx_lens=[30 + 37 * b for b in range(34)], heads=128),
 }
 
 
