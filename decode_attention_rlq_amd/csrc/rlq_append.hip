@@ -97,11 +97,14 @@ __device__ inline Dest resolve(const AppendArgs &a, int64_t tok) {
 // The same for the 16 tokens tile0 .. tile0+15, computed by one whole wave:
 // lane n < 16 gets token tile0 + n.  With fewer than 64 requests the request
 // search is one load of cu_seqlens (lane i holds cu_seqlens[i]) and 16
-// ballots, so the dependent chain is three loads long.
+// ballots, and start_pos is loaded alongside, so the dependent chain is two
+// loads long.
 __device__ inline Dest resolve_wave(const AppendArgs &a, int64_t tile0, int lane) {
   if (a.batch >= 64) return resolve(a, tile0 + (lane & 15));
   const int64_t tok = tile0 + (lane & 15);
   const int32_t cu_l = a.cu_seqlens[lane <= a.batch ? lane : a.batch];
+  // start_pos of every request, loaded alongside (lane i holds start_pos[i]).
+  const int32_t start_l = a.start_pos[lane < a.batch ? lane : a.batch - 1];
   // Request of token t = number of i in [1, batch) with cu_seqlens[i] <= t.
   int b = 0;
 #pragma unroll
@@ -110,10 +113,9 @@ __device__ inline Dest resolve_wave(const AppendArgs &a, int64_t tile0, int lane
         __builtin_amdgcn_ballot_w64(lane >= 1 && lane < a.batch && (int64_t)cu_l <= tile0 + n);
     if ((lane & 15) == n) b = __builtin_popcountll(m);
   }
-  const int32_t cu_b = __shfl(cu_l, b), cu_b1 = __shfl(cu_l, b + 1);
+  const int32_t cu_b = __shfl(cu_l, b), cu_b1 = __shfl(cu_l, b + 1), start = __shfl(start_l, b);
   Dest d{-1, 0, b, 0};
   if (tok >= a.n_tokens) return d;
-  const int32_t start = a.start_pos[b];
   d.pos = start + (int32_t)(tok - cu_b);
   d.slot = (int64_t)a.block_table[(int64_t)b * a.max_pages + (d.pos >> 6)] * RLQ_PAGE + (d.pos & 63);
   d.new_len = start + (cu_b1 - cu_b);
@@ -351,6 +353,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void append_small_kernel(AppendAr
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) ra[k][mt] = *(const u4 *)(rrow + (size_t)16 * mt * RLQ_DC + 32 * k);
     }
+    // Keep every load above the products: left to itself the scheduler
+    // interleaves them to save registers, which exposes the load latency
+    // several times over.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
