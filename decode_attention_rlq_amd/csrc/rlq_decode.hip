@@ -237,17 +237,25 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int bh, float (*wts)[16]
   const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
   constexpr int kStride = kPartialFloats / 4;
   const f4 *po = (const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats) + jp * 64 + lane;
+  // Thread (h, st) takes the (max, sum) of splits st, st + 16, ...; the first
+  // kMlKeep of them stay in registers for the second pass.  These loads go
+  // out before the partial tiles, so the statistics wait only for them.
+  // Indices past the last split load the last one (unused), so no load is
+  // followed at once by a select that would wait for it.
+  constexpr int kMlKeep = 4;
+  float2 mlv[kMlKeep];
+#pragma unroll
+  for (int u = 0; u < kMlKeep; ++u) mlv[u] = ml[min(st + 16 * u, S - 1) * 16 + h];
   f4 pre[kMergePre];
 #pragma unroll
-  for (int u = 0; u < kMergePre; ++u) {
-    const int s = grp + kMergeWaves * u;
-    pre[u] = s < S ? po[(int64_t)s * kStride] : f4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int u = 0; u < kMergePre; ++u) pre[u] = po[(int64_t)min(grp + kMergeWaves * u, S - 1) * kStride];
   {
-    // Max per head over the splits: thread (h, st) takes splits st, st + 16, ...
+    // Max per head over the splits.
     float m = kNegInf;
-#pragma unroll 4
-    for (int s = st; s < S; s += 16) m = fmaxf(m, ml[s * 16 + h].x);
+#pragma unroll
+    for (int u = 0; u < kMlKeep; ++u)
+      if (st + 16 * u < S) m = fmaxf(m, mlv[u].x);
+    for (int s = st + 16 * kMlKeep; s < S; s += 16) m = fmaxf(m, ml[s * 16 + h].x);
     red_m[st][h] = m;
   }
   __syncthreads();
@@ -255,11 +263,20 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int bh, float (*wts)[16]
     float M = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) M = fmaxf(M, red_m[i][h]);
+    const float Mc = fmaxf(M, -1e30f);  // 0 weights for empty splits
     float l = 0.f;
-#pragma unroll 4
-    for (int s = st; s < S; s += 16) {
+#pragma unroll
+    for (int u = 0; u < kMlKeep; ++u) {
+      const int s = st + 16 * u;
+      if (s < S) {
+        const float w = __builtin_amdgcn_exp2f(mlv[u].x - Mc);
+        wts[s][h] = w;
+        l += w * mlv[u].y;
+      }
+    }
+    for (int s = st + 16 * kMlKeep; s < S; s += 16) {
       const float2 v = ml[s * 16 + h];
-      const float w = __builtin_amdgcn_exp2f(v.x - fmaxf(M, -1e30f));  // 0 for empty splits
+      const float w = __builtin_amdgcn_exp2f(v.x - Mc);
       wts[s][h] = w;
       l += w * v.y;
     }
