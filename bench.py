@@ -375,8 +375,8 @@ def main():
         print(json.dumps({"copy_bytes": n, "copies": 3}))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): sharding this path "
+              "across GPUs is designed but not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -7,7 +7,7 @@ returns, so neither side can influence the other's inputs.
 
 Workload shapes follow the pages' serving setting for DeepSeek-V2-Lite
 (content latent 512, RoPE key 64, group 128; 4 concurrent requests at 256K
-input tokens) and the per-configuration recipes stated in the design doc:
+input tokens) and these per-configuration recipes:
 
   tiny            1 request x 256 tokens, 16 heads, tau 0.9816, gain 1.0
   v2lite_32k      4 x 32,768 tokens, 16 heads, paged (64-token pages)

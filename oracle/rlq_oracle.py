@@ -31,7 +31,7 @@ value, read-side rotation is folded into the absorbed query ([RoLaQ] §2.1,
 §3.3; [Figs] Fig. 1a, Fig. 3a).  Reconstruction: group mean + scale * gain *
 level ([RoLaQ] §3.2: the gain scales reconstruction around the group mean).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * scale statistic = population standard deviation of the centred group,
     two-pass, divided by the group size;
   * fixed fp32 reduction order: the adjacent-pair binary tree;
