@@ -769,8 +769,14 @@ SplitPlan plan_splits(int32_t batch, int32_t heads, int32_t max_ctx_len) {
     tps = ((ctx + kMaxSplits - 1) / kMaxSplits + RLQ_PAGE - 1) / RLQ_PAGE * RLQ_PAGE;
     splits = (ctx + tps - 1) / tps;
   }
-  // Callers reject contexts beyond kMaxSplits * kMaxSplitPages pages.
-  if (tps > (int64_t)kMaxSplitPages * RLQ_PAGE) tps = (int64_t)kMaxSplitPages * RLQ_PAGE;
+  // A split holds at most kMaxSplitPages pages (a wave pair's page ids fit
+  // one register); longer splits are cut and the count follows.  Callers
+  // reject contexts beyond kMaxSplits * kMaxSplitPages pages, so the count
+  // stays within kMaxSplits.
+  if (tps > (int64_t)kMaxSplitPages * RLQ_PAGE) {
+    tps = (int64_t)kMaxSplitPages * RLQ_PAGE;
+    splits = (ctx + tps - 1) / tps;
+  }
   return SplitPlan{(int32_t)tps, (int32_t)splits};
 }
 

@@ -74,6 +74,19 @@ def test_workspace_size(lib):
         rlq.decode_workspace_size(1, 144, 100)
 
 
+@pytest.mark.parametrize("batch,heads,ctx", [(32, 128, 59297), (1, 16, 1 << 20), (4, 16, 262144),
+                                              (256, 16, 20000), (2, 16, 5000)])
+def test_workspace_splits_cover_the_context(lib, batch, heads, ctx):
+    """The workspace holds (splits + 1) partials of 16 x 512 fp32 + 32 floats
+    per request and 16-head group, and a split covers at most 16,384 tokens:
+    the split count implied by the size must cover the longest context."""
+    per = (16 * 512 + 32) * 4
+    parts, rem = divmod(rlq.decode_workspace_size(batch, heads, ctx), per)
+    assert rem == 0
+    splits = parts // (batch * (heads // 16)) - 1
+    assert splits >= 1 and splits * 16384 >= ctx
+
+
 def test_validation_rejects_before_any_launch(lib):
     p = rlq.default_params()
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first

@@ -27,8 +27,12 @@ DECODE_CASES = {
     "h128_protect": dict(name="ragged_protect", ctx_lens=[1500, 77], heads=128),
     "tau_gain_extremes": dict(name="v2lite_32k", ctx_lens=[300, 900], tau=0.85, gain=1.2),
     # 34 requests x 8 head groups: more split workgroups than the GPU holds at
-    # once, so the merge runs as its own kernel.
+    # once.
     "wide_batch_h128": dict(name="ragged_protect", ctx_lens=[30 + 37 * b for b in range(34)], heads=128),
+    # 32 requests x 8 head groups leave one split per request by occupancy,
+    # but a split holds at most 16384 tokens: the 20,000-token request needs
+    # two.
+    "long_one_split_h128": dict(name="ragged_protect", ctx_lens=[20000] + [64] * 31, heads=128),
 }
 
 
