@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlq.so")
-SOURCES = ("rlq_host.hip", "rlq_append.hip", "rlq_decode.hip")
+SOURCES = ("rlq_host.hip", "rlq_append.hip", "rlq_decode.hip", "rlq_decode_wide.hip")
 
 # Packed fp32 VALU ops are kept out of the generated code: hipcc would form
 # them from ordinary float code, and the kernels do not need them.

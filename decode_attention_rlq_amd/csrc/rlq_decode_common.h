@@ -1,0 +1,261 @@
+// Device helpers shared by the decode kernels (16-head split kernel and the
+// many-head kernel): the contraction order of the content coordinates, the
+// fp16 c_hat layout in LDS, the decoding of 2-bit codes through a per-token
+// table of four values, and the LSE merge of split partials.
+// RoLaQ paper: §3.2 (reconstruction = group mean + scale * gain * level),
+// §2.1 / §3.3 (absorbed decode over the shared latent), §4.1 / §A.3 (BF16
+// sink and recent tokens).
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "rlq_internal.h"
+
+namespace rlq {
+namespace {
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kPageTok = 64;                        // tokens per page
+constexpr int kWaveTok = 32;                        // tokens per tile
+constexpr int kSubBytes = kTile * (RLQ_DC / 2) * 2; // 8 KB: fp16 c_hat half of 16 tokens
+constexpr int kWaveBytes = 2 * kSubBytes;           // 16 KB: fp16 c_hat half of one tile
+// Lazy online softmax: the running max m is raised only when a tile's max
+// exceeds it by more than kLazy (log2 units); P = 2^(s - m + kBias) then
+// stays at most 2^15, inside fp16's range.
+constexpr float kLazy = 8.f;
+constexpr float kBias = 15.f - kLazy;
+
+// Contraction order of the content coordinates (shared by the query layout,
+// the code decoding, the LDS layout and the output mapping).  K-step k
+// (0..15), lane group g (lane / 16) and operand slot j (0..7) of the
+// 16x16x32 MFMA cover latent coordinate  16 * word(k, g) + sub(j, k & 1):
+//   word(k, g) = 4 * (q0(g) + 2 * (k >> 3)) + ((k >> 1) & 3),
+//   q0(g)      = 4 * (g >> 1) + (g & 1)        (16-byte run of code words),
+//   sub(j, h)  = 2h + (j >> 2) + 4 * (j & 3)   (code within the word).
+// A lane thus reads code words [4 q0, 4 q0 + 4) and [4 q0 + 8, 4 q0 + 12) of
+// its token: groups 2*(g>>1) (k < 8) and 2*(g>>1)+1 (k >= 8).
+__device__ __host__ constexpr int coord_of(int k, int g, int j) {
+  return 16 * (4 * ((4 * (g >> 1) + (g & 1)) + 2 * (k >> 3)) + ((k >> 1) & 3)) +
+         2 * (k & 1) + (j >> 2) + 4 * (j & 3);
+}
+
+// LDS slot (16 bytes) of token row r written by lane group g at K-step k.
+// LDS has 64 four-byte banks (256 bytes per cycle): a 16-byte write serves 16
+// lanes per cycle, an 8-byte transposed read 32 lanes.  The xor moves odd
+// K-steps to the other 128-byte half of each 256-byte window, so the 32 lanes
+// of a transposed read (tokens 0-7 of one writer lane group, K-steps 2p and
+// 2p+1, both 8-byte halves) cover all 64 banks once.
+__device__ __host__ constexpr int chat_slot(int k, int g, int r) {
+  return (16 * g + r) ^ (8 * (k & 1));
+}
+
+// Value tile jp (0..31) holds, in row m = 4q + e (q, e in 0..3), the latent
+// coordinate in K-step 2*(jp>>2) + (q>>1), lane group jp&3, slot 4*(q&1)+e.
+__device__ __host__ constexpr int value_coord(int jp, int m) {
+  return coord_of(2 * (jp >> 2) + ((m >> 2) >> 1), jp & 3, 4 * ((m >> 2) & 1) + (m & 3));
+}
+
+__device__ inline uint32_t h16(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ inline float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// Reductions over the 4 lane groups sharing lane & 15 (xor 16, xor 32).
+__device__ inline float max_over_groups(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_over_groups(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Table of one (token, group): low bytes and high bytes of the four fp16
+// values, so v_perm_b32 can look both up with 2-bit selectors.
+struct Lut {
+  uint32_t lo, hi;
+};
+__device__ inline Lut make_lut(float mu, float s, float gain, float a, float b, bool valid) {
+  const float sg = s * gain;
+  const uint32_t p01 = h16(mu - sg * b) | (h16(mu - sg * a) << 16);
+  const uint32_t p23 = h16(mu + sg * a) | (h16(mu + sg * b) << 16);
+  Lut l;
+  l.lo = valid ? __builtin_amdgcn_perm(p23, p01, 0x06040200u) : 0u;
+  l.hi = valid ? __builtin_amdgcn_perm(p23, p01, 0x07050301u) : 0u;
+  return l;
+}
+
+// Codes 2h, 2h+4, 2h+8, 2h+12, 2h+1, 2h+5, 2h+9, 2h+13 of word w as eight
+// fp16 values (operand slots 0..7).
+__device__ inline u4 decode8(uint32_t w, int h, const Lut &l) {
+  const uint32_t y0 = (w >> (4 * h)) & 0x03030303u;
+  const uint32_t y1 = (w >> (4 * h + 2)) & 0x03030303u;
+  const uint32_t lo0 = __builtin_amdgcn_perm(0u, l.lo, y0);
+  const uint32_t hi0 = __builtin_amdgcn_perm(0u, l.hi, y0);
+  const uint32_t lo1 = __builtin_amdgcn_perm(0u, l.lo, y1);
+  const uint32_t hi1 = __builtin_amdgcn_perm(0u, l.hi, y1);
+  u4 r;
+  r[0] = __builtin_amdgcn_perm(hi0, lo0, 0x05010400u);
+  r[1] = __builtin_amdgcn_perm(hi0, lo0, 0x07030602u);
+  r[2] = __builtin_amdgcn_perm(hi1, lo1, 0x05010400u);
+  r[3] = __builtin_amdgcn_perm(hi1, lo1, 0x07030602u);
+  return r;
+}
+
+// The same eight coordinates taken from a BF16 latent word (16 values held
+// in two 16-byte vectors), converted to fp16.
+__device__ inline u4 convert8(const u4 &w0, const u4 &w1, int h) {
+  auto elem = [&](int e) -> uint32_t {
+    const uint32_t v = (e < 8) ? w0[e >> 1] : w1[(e - 8) >> 1];
+    return (e & 1) ? (v >> 16) : (v & 0xFFFFu);
+  };
+  u4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int j0 = 2 * p, j1 = 2 * p + 1;
+    const int e0 = 2 * h + (j0 >> 2) + 4 * (j0 & 3);
+    const int e1 = 2 * h + (j1 >> 2) + 4 * (j1 & 3);
+    r[p] = h16(bf16_to_f32(elem(e0))) | (h16(bf16_to_f32(elem(e1))) << 16);
+  }
+  return r;
+}
+
+struct Protect {
+  int ns, nr;  // protected prefix length and recent length inside [0, ctx)
+};
+
+__device__ inline Protect protect_range(const DecodeArgs &A, int ctx) {
+  Protect p;
+  p.ns = (A.sink != nullptr) ? min(A.n_sink, ctx) : 0;
+  p.nr = (A.recent != nullptr) ? min(A.n_recent, ctx - p.ns) : 0;
+  return p;
+}
+
+template <bool V>
+using bool_c = std::integral_constant<bool, V>;
+
+// LSE merge of the split partials of one (request b, 16-head tile ht) for
+// value tile `jp` (16 heads x 16 latent coordinates as 64 lanes x 4) by a
+// workgroup of four waves: wave w sums splits w, w + 4, ..., then the four
+// sums are added in a fixed order.  Each wave loads its first kMergePre
+// partial tiles before the statistics pass, so their latency overlaps it.
+constexpr int kMergeWaves = 4;
+constexpr int kMergePre = 16;
+
+// Where the partials of one (request, head tile) are: S splits, each a
+// 16 x 512 fp32 tile in the accumulator's order (po, f4 units) and 16
+// (max, sum) pairs (ml), consecutive splits po_stride / ml_stride apart.
+struct MergeSrc {
+  const f4 *po;
+  int64_t po_stride;
+  const float2 *ml;
+  int ml_stride;
+  int S;
+};
+
+__device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const MergeSrc &src,
+                           float (*wts)[16], float (*red_m)[16], float (*red_l)[16], f4 (*part)[64]) {
+  const int S = src.S;
+  const float2 *ml = src.ml;
+  const int mls = src.ml_stride;
+  const int tid = threadIdx.x;
+  const int h = tid & 15, st = tid >> 4;
+  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
+  const int64_t ps = src.po_stride;
+  const f4 *po = src.po + jp * 64 + lane;
+  // Thread (h, st) takes the (max, sum) of splits st, st + 16, ...; the first
+  // kMlKeep of them stay in registers for the second pass.  These loads go
+  // out before the partial tiles, so the statistics wait only for them.
+  // Indices past the last split load the last one (unused), so no load is
+  // followed at once by a select that would wait for it.  S >= 1.
+  constexpr int kMlKeep = 4;
+  float2 mlv[kMlKeep];
+#pragma unroll
+  for (int u = 0; u < kMlKeep; ++u) mlv[u] = ml[min(st + 16 * u, S - 1) * mls + h];
+  f4 pre[kMergePre];
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u) pre[u] = po[(int64_t)min(grp + kMergeWaves * u, S - 1) * ps];
+  {
+    // Max per head over the splits.
+    float m = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kMlKeep; ++u)
+      if (st + 16 * u < S) m = fmaxf(m, mlv[u].x);
+    for (int s = st + 16 * kMlKeep; s < S; s += 16) m = fmaxf(m, ml[s * mls + h].x);
+    red_m[st][h] = m;
+  }
+  __syncthreads();
+  {
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, red_m[i][h]);
+    const float Mc = fmaxf(M, -1e30f);  // 0 weights for empty splits
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMlKeep; ++u) {
+      const int s = st + 16 * u;
+      if (s < S) {
+        const float w = __builtin_amdgcn_exp2f(mlv[u].x - Mc);
+        wts[s][h] = w;
+        l += w * mlv[u].y;
+      }
+    }
+    for (int s = st + 16 * kMlKeep; s < S; s += 16) {
+      const float2 v = ml[s * mls + h];
+      const float w = __builtin_amdgcn_exp2f(v.x - Mc);
+      wts[s][h] = w;
+      l += w * v.y;
+    }
+    red_l[st][h] = l;
+  }
+  __syncthreads();
+  {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+      const int s = grp + kMergeWaves * u;
+      if (s < S) acc += wts[s][hh] * pre[u];
+    }
+    int s = grp + kMergeWaves * kMergePre;
+    for (; s + 7 * kMergeWaves < S; s += 8 * kMergeWaves) {
+      f4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = po[(int64_t)(s + kMergeWaves * u) * ps];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wts[s + kMergeWaves * u][hh] * v[u];
+    }
+    for (; s < S; s += kMergeWaves) acc += wts[s][hh] * po[(int64_t)s * ps];
+    part[grp][lane] = acc;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) L += red_l[i][hh];
+    float Mh = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
+    const f4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
+    if (A.lse != nullptr && jp == 0 && lane < 16)
+      A.lse[(int64_t)b * A.heads + ht * 16 + lane] =
+          L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+  }
+}
+
+}  // namespace
+}  // namespace rlq

@@ -139,7 +139,9 @@ int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_
   if (bytes == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16 ||
       max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX)
     return RLQ_EINVAL;
-  *bytes = rlq::decode_workspace_bytes(batch, heads, rlq::plan_splits(batch, heads, max_ctx_len));
+  *bytes = rlq::use_wide(heads)
+               ? rlq::wide_workspace_bytes(batch, heads, rlq::plan_wide(batch, heads, max_ctx_len))
+               : rlq::decode_workspace_bytes(batch, heads, rlq::plan_splits(batch, heads, max_ctx_len));
   return RLQ_OK;
 }
 
@@ -164,8 +166,12 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
       !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
       (lse != nullptr && !aligned(lse, 4)))
     return RLQ_EINVAL;
+  const bool wide = rlq::use_wide(heads);
   const rlq::SplitPlan plan = rlq::plan_splits(batch, heads, max_ctx_len);
-  if (workspace_bytes < rlq::decode_workspace_bytes(batch, heads, plan)) return RLQ_ENOSPC;
+  const rlq::WidePlan wplan = rlq::plan_wide(batch, heads, max_ctx_len);
+  const size_t need = wide ? rlq::wide_workspace_bytes(batch, heads, wplan)
+                           : rlq::decode_workspace_bytes(batch, heads, plan);
+  if (workspace_bytes < need) return RLQ_ENOSPC;
   st = check_device();
   if (st != RLQ_OK) return st;
 
@@ -190,11 +196,24 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   a.gain = p->gain;
   a.level_inner = p->level_inner;
   a.level_outer = p->level_outer;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.max_ctx_len = max_ctx_len;
+  a.item_slots = wplan.item_slots;
+  a.item_target = wplan.item_target;
+  if (wide) {
+    // Many heads: balanced work items, each 32-token tile decoded once per 64 heads.
+    const size_t parts = (size_t)wplan.item_slots * (heads / 16);
+    a.part_o = (float *)workspace;
+    a.part_ml = a.part_o + parts * rlq::kPartialFloats;
+    a.plan = (int32_t *)(a.part_ml + parts * 32);
+    return hip_status(rlq::launch_decode_wide(a, batch, (hipStream_t)stream));
+  }
   const size_t parts = (size_t)batch * (heads / 16) * (plan.splits + a.prot);
   a.part_o = (float *)workspace;
   a.part_ml = a.part_o + parts * rlq::kPartialFloats;
-  a.out = out;
-  a.lse = lse;
+  a.plan = nullptr;
   return hip_status(rlq::launch_decode(a, batch, (hipStream_t)stream));
 }
 

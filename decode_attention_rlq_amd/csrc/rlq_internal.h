@@ -82,6 +82,12 @@ struct DecodeArgs {
   float *part_ml;  // [B][HG][S+prot][16][2]
   float *out;      // [B][H][512]
   float *lse;      // [B][H] or null
+  // Many-head path (heads a multiple of kWideHeads) only.
+  int32_t batch;
+  int32_t max_ctx_len;
+  int32_t item_slots;   // workgroups per 64-head group: work items at most
+  int32_t item_target;  // work items the balanced plan aims for
+  int32_t *plan;        // [B][2]: first work item and item count of each request
 };
 
 // Split policy shared by the workspace query and the launch.
@@ -94,5 +100,23 @@ SplitPlan plan_splits(int32_t batch, int32_t heads, int32_t max_ctx_len);
 size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &plan);
 
 hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream);
+
+// Many-head path: heads per workgroup, workgroups resident at once (one per
+// CU), and the bounds of a work item (a run of 32-token tiles of one request).
+constexpr int kWideHeads = 64;
+constexpr int kResidentWide = 256;
+constexpr int kMinItemTiles = 16;
+constexpr int kMaxItemPages = 1024;
+constexpr int kMaxItemTiles = 2 * (kMaxItemPages - 1);
+
+inline bool use_wide(int32_t heads) { return heads % kWideHeads == 0; }
+
+struct WidePlan {
+  int32_t item_slots;
+  int32_t item_target;
+};
+WidePlan plan_wide(int32_t batch, int32_t heads, int32_t max_ctx_len);
+size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan);
+hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t stream);
 
 }  // namespace rlq

@@ -74,7 +74,7 @@ def test_workspace_size(lib):
         rlq.decode_workspace_size(1, 144, 100)
 
 
-@pytest.mark.parametrize("batch,heads,ctx", [(32, 128, 59297), (1, 16, 1 << 20), (4, 16, 262144),
+@pytest.mark.parametrize("batch,heads,ctx", [(32, 112, 59297), (1, 16, 1 << 20), (4, 16, 262144),
                                               (256, 16, 20000), (2, 16, 5000)])
 def test_workspace_splits_cover_the_context(lib, batch, heads, ctx):
     """The workspace holds (splits + 1) partials of 16 x 512 fp32 + 32 floats
@@ -85,6 +85,25 @@ def test_workspace_splits_cover_the_context(lib, batch, heads, ctx):
     assert rem == 0
     splits = parts // (batch * (heads // 16)) - 1
     assert splits >= 1 and splits * 16384 >= ctx
+
+
+@pytest.mark.parametrize("batch,heads,ctx", [(32, 128, 59297), (4, 64, 262144), (1, 128, 1 << 22),
+                                              (200, 128, 1000), (3, 128, 0), (300, 64, 70000)])
+def test_workspace_many_heads_holds_every_item(lib, batch, heads, ctx):
+    """With a multiple of 64 heads the workspace holds, per work-item slot and
+    16-head tile, a 16 x 512 fp32 partial + 32 floats, then two ints per
+    request.  The slots cover one round of workgroups (256 per 64 heads),
+    and at least ceil(tiles / 2046) items per request (an item spans at most
+    2046 tiles of 32 tokens), in a multiple of 8."""
+    per = (16 * 512 + 32) * 4
+    size = rlq.decode_workspace_size(batch, heads, ctx)
+    parts, rem = divmod(size - 8 * batch, per)
+    assert rem == 0 and parts % (heads // 16) == 0
+    slots = parts // (heads // 16)
+    tiles = -(-ctx // 32)
+    assert slots % 8 == 0
+    assert slots >= 256 // (heads // 64)
+    assert slots >= batch * max(1, -(-tiles // 2046))
 
 
 def test_validation_rejects_before_any_launch(lib):
