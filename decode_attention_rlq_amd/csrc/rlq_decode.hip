@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
   const int bh = blockIdx.y, S = A.splits + A.prot;
   const MergeSrc src{(const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats), kPartialFloats / 4,
                      (const float2 *)(A.part_ml + (int64_t)bh * S * 32), 16, S};
-  merge_tile(A, blockIdx.x, bh / HG, bh % HG, src, wts, red_m, red_l, part);
+  merge_tiles(A, blockIdx.x, 1, bh / HG, bh % HG, src, wts, red_m, red_l, part);
 }
 
 }  // namespace

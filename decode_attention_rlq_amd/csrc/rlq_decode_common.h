@@ -146,10 +146,12 @@ template <bool V>
 using bool_c = std::integral_constant<bool, V>;
 
 // LSE merge of the split partials of one (request b, 16-head tile ht) for
-// value tile `jp` (16 heads x 16 latent coordinates as 64 lanes x 4) by a
-// workgroup of four waves: wave w sums splits w, w + 4, ..., then the four
-// sums are added in a fixed order.  Each wave loads its first kMergePre
-// partial tiles before the statistics pass, so their latency overlaps it.
+// value tiles jp0 .. jp0 + njp - 1 (each 16 heads x 16 latent coordinates as
+// 64 lanes x 4) by a workgroup of four waves.  The (max, sum) statistics are
+// reduced once; then, per value tile, wave w sums splits w, w + 4, ..., and
+// the four sums are added in a fixed order.  The first kMergePre partial tiles
+// of each value tile are loaded ahead (before the statistics pass for the
+// first, during the previous tile's reduction for the others).
 constexpr int kMergeWaves = 4;
 constexpr int kMergePre = 16;
 
@@ -164,8 +166,8 @@ struct MergeSrc {
   int S;
 };
 
-__device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const MergeSrc &src,
-                           float (*wts)[16], float (*red_m)[16], float (*red_l)[16], f4 (*part)[64]) {
+__device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht, const MergeSrc &src,
+                            float (*wts)[16], float (*red_m)[16], float (*red_l)[16], f4 (*part)[64]) {
   const int S = src.S;
   const float2 *ml = src.ml;
   const int mls = src.ml_stride;
@@ -173,7 +175,6 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const Mer
   const int h = tid & 15, st = tid >> 4;
   const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
   const int64_t ps = src.po_stride;
-  const f4 *po = src.po + jp * 64 + lane;
   // Thread (h, st) takes the (max, sum) of splits st, st + 16, ...; the first
   // kMlKeep of them stay in registers for the second pass.  These loads go
   // out before the partial tiles, so the statistics wait only for them.
@@ -184,8 +185,12 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const Mer
 #pragma unroll
   for (int u = 0; u < kMlKeep; ++u) mlv[u] = ml[min(st + 16 * u, S - 1) * mls + h];
   f4 pre[kMergePre];
+  auto prefetch = [&](int jp) {
+    const f4 *po = src.po + jp * 64 + lane;
 #pragma unroll
-  for (int u = 0; u < kMergePre; ++u) pre[u] = po[(int64_t)min(grp + kMergeWaves * u, S - 1) * ps];
+    for (int u = 0; u < kMergePre; ++u) pre[u] = po[(int64_t)min(grp + kMergeWaves * u, S - 1) * ps];
+  };
+  prefetch(jp0);
   {
     // Max per head over the splits.
     float m = kNegInf;
@@ -220,7 +225,18 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const Mer
     red_l[st][h] = l;
   }
   __syncthreads();
-  {
+  float L = 0.f, Mh = kNegInf;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) L += red_l[i][hh];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
+  for (int t = 0; t < njp; ++t) {
+    const int jp = jp0 + t;
+    const f4 *po = src.po + jp * 64 + lane;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kMergePre; ++u) {
@@ -236,24 +252,18 @@ __device__ void merge_tile(const DecodeArgs &A, int jp, int b, int ht, const Mer
       for (int u = 0; u < 8; ++u) acc += wts[s + kMergeWaves * u][hh] * v[u];
     }
     for (; s < S; s += kMergeWaves) acc += wts[s][hh] * po[(int64_t)s * ps];
+    if (t + 1 < njp) prefetch(jp + 1);
     part[grp][lane] = acc;
-  }
-  __syncthreads();
-  if (grp == 0) {
-    float L = 0.f;
+    __syncthreads();
+    if (grp == 0) {
+      const f4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) L += red_l[i][hh];
-    float Mh = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
-    const f4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
-    if (A.lse != nullptr && jp == 0 && lane < 16)
-      A.lse[(int64_t)b * A.heads + ht * 16 + lane] =
-          L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+      for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
+      if (A.lse != nullptr && jp == 0 && lane < 16)
+        A.lse[(int64_t)b * A.heads + ht * 16 + lane] =
+            L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+    }
+    if (t + 1 < njp) __syncthreads();  // part is rewritten by the next tile
   }
 }
 

@@ -161,6 +161,8 @@ __device__ inline int fill_slot(int W, int e, int st, int r) {
 // distinct bank groups.
 __device__ inline int rope_off(int t, int c) { return t * 128 + 16 * (c ^ ((t >> 1) & 7)); }
 
+// kProt: the cache has sink and/or recent BF16 rows.
+template <bool kProt>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int x = blockIdx.x, hq = blockIdx.y;  // work item, 64-head group
@@ -227,51 +229,69 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   const int ftok = 16 * fst + fr;  // token within the tile
   // RoPE copy role: token 4 * wave + (lane >> 4), bytes 8 * (lane & 15) ...
   const int rtok = 4 * wave + (lane >> 4), ru = lane & 15;
-  auto tile_slot0 = [&](int i) -> int64_t {  // cache slot of the tile's first token
-    const int tt = it.tb + min(i, n - 1);      // past the end: the last tile again
-    return (int64_t)pg[(tt >> 1) - pg0] * RLQ_PAGE + 32 * (tt & 1);
+  // Cache slot of the tile's first token: the page id is read from the LDS
+  // table and kept in a scalar register, so every fill load is a scalar row
+  // base plus a 32-bit lane offset.
+  auto tile_slot0 = [&](int i) -> int64_t {
+    const int tt = it.tb + min(i, n - 1);  // past the end: the last tile again
+    const int page = __builtin_amdgcn_readfirstlane(pg[(tt >> 1) - pg0]);
+    return (int64_t)page * RLQ_PAGE + 32 * (tt & 1);
   };
+  const uint32_t off_cw = (uint32_t)(ftok * RLQ_WORDS + W0);  // words
+  const uint32_t off_mt = (uint32_t)(ftok * 8 + fgrp);        // floats
+  const uint32_t off_rp = (uint32_t)(rtok * RLQ_DR + 4 * ru); // bf16 elements
   auto load_fill = [&](int i, FillLoad &F) {
     const int64_t s0 = tile_slot0(i);
-    const int64_t sf = s0 + ftok;
-    F.cw = *(const u2 *)(A.codes + sf * RLQ_WORDS + W0);
-    F.mu = A.meta[sf * 8 + fgrp];
-    F.sd = A.meta[sf * 8 + 4 + fgrp];
-    F.rp = *(const u2 *)(A.rope + (s0 + rtok) * RLQ_DR + 4 * ru);
+    const uint32_t *cw = A.codes + s0 * RLQ_WORDS;
+    const float *mt = A.meta + s0 * 8;
+    const uint16_t *rp = A.rope + s0 * RLQ_DR;
+    F.cw = *(const u2 *)(cw + off_cw);
+    F.mu = mt[off_mt];
+    F.sd = mt[off_mt + 4];
+    F.rp = *(const u2 *)(rp + off_rp);
   };
-  auto cbuf = [&](int i) -> unsigned char * { return smem + (i % kBufs) * kCBufBytes; };
-  auto rbuf = [&](int i) -> unsigned char * {
-    return smem + kBufs * kCBufBytes + (i % kBufs) * kRopeBufBytes;
+  // c_hat and RoPE buffers of ring slot k (tile i lives in slot i % 3).
+  auto cbuf = [&](int k) -> unsigned char * { return smem + k * kCBufBytes; };
+  auto rbuf = [&](int k) -> unsigned char * { return smem + kBufs * kCBufBytes + k * kRopeBufBytes; };
+  // Fill of tile i (into ring slot k) in parts, so the iteration can
+  // interleave its decoding with the MFMAs: the table (fill_lut), the four
+  // 16-byte slots (fill_part), then the RoPE copy and, in tiles that hold sink
+  // or recent positions, the BF16 latents of those tokens written over the
+  // decoded values (fill_end).
+  auto fill_lut = [&](int i, const FillLoad &F) -> Lut {
+    const int pos = kWaveTok * (it.tb + i) + ftok;
+    return make_lut(F.mu, F.sd, A.gain, A.level_inner, A.level_outer, pos < ctx);
   };
-  auto fill = [&](int i, const FillLoad &F) {
-    const int pos0 = kWaveTok * (it.tb + i);
-    const int pos = pos0 + ftok;
-    unsigned char *cb = cbuf(i);
-    const bool valid = pos < ctx;
-    const Lut l = make_lut(F.mu, F.sd, A.gain, A.level_inner, A.level_outer, valid);
-    u4 v[4];
+  auto fill_part = [&](int k, const FillLoad &F, const Lut &l, int e2) {
+    *(u4 *)(cbuf(k) + fill_slot(W0 + (e2 >> 1), e2 & 1, fst, fr)) = decode8(F.cw[e2 >> 1], e2 & 1, l);
+  };
+  auto fill_end = [&](int i, int k, const FillLoad &F) {
+    // RoPE key: 8 bytes of token rtok, chunk ru >> 1.
+    *(u2 *)(rbuf(k) + rope_off(rtok, ru >> 1) + 8 * (ru & 1)) = F.rp;
+    if constexpr (kProt) {
+      const int pos0 = kWaveTok * (it.tb + i);
+      if (pos0 < pt.ns || pos0 + kWaveTok > ctx - pt.nr) {
+        const int pos = pos0 + ftok;
+        const bool sink = pos < pt.ns, rec = pos >= ctx - pt.nr && pos < ctx;
+        if (sink || rec) {
+          const uint16_t *row = sink ? A.sink + ((int64_t)b * A.n_sink + pos) * RLQ_DC
+                                     : A.recent + ((int64_t)b * A.n_recent + pos % A.n_recent) * RLQ_DC;
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) v[e2] = decode8(F.cw[e2 >> 1], e2 & 1, l);
-    // Tiles that hold sink or recent positions: those tokens take their
-    // BF16 latent (same operand order) instead of the codes.
-    if (pos0 < pt.ns || pos0 + kWaveTok > ctx - pt.nr) {
-      const bool sink = pos < pt.ns, rec = pos >= ctx - pt.nr && pos < ctx;
-      if (sink || rec) {
-        const uint16_t *row = sink ? A.sink + ((int64_t)b * A.n_sink + pos) * RLQ_DC
-                                   : A.recent + ((int64_t)b * A.n_recent + pos % A.n_recent) * RLQ_DC;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const u4 w0 = *(const u4 *)(row + 16 * (W0 + w));
-          const u4 w1 = *(const u4 *)(row + 16 * (W0 + w) + 8);
-          v[2 * w] = convert8(w0, w1, 0);
-          v[2 * w + 1] = convert8(w0, w1, 1);
+          for (int w = 0; w < 2; ++w) {
+            const u4 w0 = *(const u4 *)(row + 16 * (W0 + w));
+            const u4 w1 = *(const u4 *)(row + 16 * (W0 + w) + 8);
+            *(u4 *)(cbuf(k) + fill_slot(W0 + w, 0, fst, fr)) = convert8(w0, w1, 0);
+            *(u4 *)(cbuf(k) + fill_slot(W0 + w, 1, fst, fr)) = convert8(w0, w1, 1);
+          }
         }
       }
     }
+  };
+  auto fill = [&](int i, int k, const FillLoad &F) {
+    const Lut l = fill_lut(i, F);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) *(u4 *)(cb + fill_slot(W0 + (e2 >> 1), e2 & 1, fst, fr)) = v[e2];
-    // RoPE key: 8 bytes of token rtok, chunk ru >> 1.
-    *(u2 *)(rbuf(i) + rope_off(rtok, ru >> 1) + 8 * (ru & 1)) = F.rp;
+    for (int e2 = 0; e2 < 4; ++e2) fill_part(k, F, l, e2);
+    fill_end(i, k, F);
   };
 
   // ---- pair state
@@ -296,6 +316,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     sc[0] = h == 0 ? acc_prev[0] + o0 : o0 + acc_prev[0];
     sc[1] = h == 0 ? acc_prev[1] + o1 : o1 + acc_prev[1];
     // sc[st][j] = raw score of position c0 + 16*st + 4*g4 + j, head r16.
+    // Positions past the context score -inf.
     if (c0 + kWaveTok > ctx) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -321,9 +342,17 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
       }
     };
     exps();
-    float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mt = max_over_groups(mt) * A.scale_log2;
+    // Tile max with v_med3 (med3(x, y, +inf) = max(x, y)): the scores are
+    // finite or -inf here, so no NaN handling is needed.
+    auto mx = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, __builtin_inff()); };
+    float mt = mx(mx(mx(sc[0][0], sc[0][1]), mx(sc[0][2], sc[0][3])),
+                  mx(mx(sc[1][0], sc[1][1]), mx(sc[1][2], sc[1][3])));
+    {
+      auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = mx(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = mx(__uint_as_float(c[0]), __uint_as_float(c[1])) * A.scale_log2;
+    }
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -354,16 +383,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
       O[4 * p + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[q], PB, O[4 * p + q], 0, 0, 0);
   };
 
-  // Iteration i: partner's partial of tile i-1 -> softmax -> value product of
-  // tile i-1 (c_hat buffer i-1), partial scores of tile i (buffer i), fill of
-  // tile i+1 (buffer i+1) from loads issued three tiles ahead; then this
-  // wave's partial of tile i goes to the exchange slots and the barrier
-  // closes the iteration.  kScore / kValue switch the first and last halves.
-  auto iteration = [&](auto score_c, auto value_c, int i, FillLoad &F) {
+  // Iteration i (tile i in ring slot k = i % 3, a constant in each unrolled
+  // copy): partner's partial of tile i-1 -> softmax -> value product of tile
+  // i-1 (slot k+2), partial scores of tile i (slot k), and the fill of tile
+  // i+1 (slot k+1) from loads issued three tiles ahead, its four parts placed
+  // between the MFMA groups; then this wave's partial of tile i goes to the
+  // exchange slots, the loads of tile i+4 are issued and the barrier closes
+  // the iteration.  Past the item's end the fill repeats its last tile into a
+  // free slot, so every scoring iteration issues the same loads.  kScore /
+  // kValue switch off the first and last halves.
+  auto iteration = [&](auto score_c, auto value_c, int i, int k, FillLoad &F) {
     constexpr bool kScore = decltype(score_c)::value;
     constexpr bool kValue = decltype(value_c)::value;
-    const unsigned char *cw = cbuf(i) + h * kWaveBytes;       // tile i, this wave's half
-    const unsigned char *vw = cbuf(i + 2) + h * kWaveBytes;   // tile i-1 (i + 2 = i - 1 mod 3)
+    const int kn = k == 2 ? 0 : k + 1, kp = k == 0 ? 2 : k - 1;
+    const unsigned char *cw = cbuf(k) + h * kWaveBytes;   // tile i, this wave's half
+    const unsigned char *vw = cbuf(kp) + h * kWaveBytes;  // tile i-1
     f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
     auto score_pair = [&](int p) {
 #pragma unroll
@@ -374,6 +408,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
           acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), qB[kl], acc[st], 0, 0, 0);
         }
     };
+    Lut fl;
+    if constexpr (kScore) fl = fill_lut(i + 1, F);
     half8 av0[4];
     if constexpr (kValue) {
       const f4 *other = xch_at(i - 1, h ^ 1);
@@ -390,47 +426,57 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
       half8 av[4];
       if constexpr (kValue) tr_pair(vw, p, av);
       if constexpr (kScore) score_pair(p);
+      if constexpr (kScore) fill_part(kn, F, fl, p - 1);
       if constexpr (kValue) value_pair(p, av);
     }
     if constexpr (kScore) {
-      const unsigned char *rb = rbuf(i);
+      const unsigned char *rb = rbuf(k);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const u4 rp = *(const u4 *)(rb + rope_off(16 * st + r16, 2 * g4 + h));
         acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp), qrB, acc[st], 0, 0, 0);
       }
-      if (i + 1 < n) {
-        fill(i + 1, F);
-        load_fill(i + 4, F);
-      }
+      fill_part(kn, F, fl, 3);
+      fill_end(i + 1, kn, F);
       f4 *mine = xch_at(i, h);
       mine[lane] = acc[0];
       mine[64 + lane] = acc[1];
       acc_prev[0] = acc[0];
       acc_prev[1] = acc[1];
+      __builtin_amdgcn_sched_barrier(0);
+      load_fill(i + 4, F);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     }
   };
 
   if (n > 0) {
+    // The ring's loads are pinned in issue order (scheduling barriers).
     FillLoad F0, F1, F2;
     load_fill(0, F0);
+    __builtin_amdgcn_sched_barrier(0);
     load_fill(1, F1);
+    __builtin_amdgcn_sched_barrier(0);
     load_fill(2, F2);
-    fill(0, F0);
+    __builtin_amdgcn_sched_barrier(0);
+    fill(0, 0, F0);
     load_fill(3, F0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    // Iteration i fills tile i+1 from buffer (i+1) % 3 and reloads it with
-    // tile i+4.
-    iteration(bool_c<true>{}, bool_c<false>{}, 0, F1);
-    for (int i = 1; i < n; i += 3) {
-      iteration(bool_c<true>{}, bool_c<true>{}, i, F2);
-      if (i + 1 >= n) break;
-      iteration(bool_c<true>{}, bool_c<true>{}, i + 1, F0);
-      if (i + 2 >= n) break;
-      iteration(bool_c<true>{}, bool_c<true>{}, i + 2, F1);
+    // Iteration i fills tile i+1 from ring entry (i+1) % 3 and reloads it
+    // with tile i+4.  Whole rounds of three run in the loop (no exit inside
+    // it, which keeps the compiler's load-wait counts exact at its head), the
+    // remaining one or two after it.
+    iteration(bool_c<true>{}, bool_c<false>{}, 0, 0, F1);
+    const int n3 = 1 + (n - 1) / 3 * 3;
+    for (int i = 1; i < n3; i += 3) {
+      iteration(bool_c<true>{}, bool_c<true>{}, i, 1, F2);
+      iteration(bool_c<true>{}, bool_c<true>{}, i + 1, 2, F0);
+      iteration(bool_c<true>{}, bool_c<true>{}, i + 2, 0, F1);
     }
-    iteration(bool_c<false>{}, bool_c<true>{}, n, F0);
+    if (n3 < n) iteration(bool_c<true>{}, bool_c<true>{}, n3, 1, F2);
+    if (n3 + 1 < n) iteration(bool_c<true>{}, bool_c<true>{}, n3 + 1, 2, F0);
+    iteration(bool_c<false>{}, bool_c<true>{}, n, n % kBufs, F0);
   }
 
   // ---- partial of this pair's head tile: wave h writes latent half h.
@@ -449,8 +495,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   }
 }
 
-// Merge of the items of one request: 32 workgroups of 4 waves per (request,
-// 16-head tile); the request's items are consecutive.
+// Merge of the items of one request: gridDim.x workgroups of 4 waves per
+// (request, 16-head tile), each for 32 / gridDim.x of the 32 value tiles (so a
+// large batch has fewer, longer workgroups); the request's items are
+// consecutive.
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(DecodeArgs A) {
   __shared__ float wts[kMaxSplits + 1][16];
   __shared__ float red_m[16][16], red_l[16][16];
@@ -461,7 +509,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(Dec
   const int64_t p0 = (int64_t)first * HT + ht;
   const MergeSrc src{(const f4 *)(A.part_o + p0 * kPartialFloats), (int64_t)HT * (kPartialFloats / 4),
                      (const float2 *)(A.part_ml + p0 * 32), HT * 16, count};
-  merge_tile(A, blockIdx.x, b, ht, src, wts, red_m, red_l, part);
+  const int njp = 32 / gridDim.x;
+  merge_tiles(A, blockIdx.x * njp, njp, b, ht, src, wts, red_m, red_l, part);
 }
 
 }  // namespace
@@ -491,17 +540,24 @@ size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan) 
 hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_wide_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
-    if (e != hipSuccess) return e;
+    for (const void *f : {(const void *)decode_wide_kernel<false>, (const void *)decode_wide_kernel<true>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   const dim3 grid(a.item_slots, a.heads / kWideHeads);
-  hipLaunchKernelGGL(decode_wide_kernel, grid, dim3(kDecodeThreads), kWideLds, stream, a);
+  if (a.prot)
+    hipLaunchKernelGGL(decode_wide_kernel<true>, grid, dim3(kDecodeThreads), kWideLds, stream, a);
+  else
+    hipLaunchKernelGGL(decode_wide_kernel<false>, grid, dim3(kDecodeThreads), kWideLds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_wide_merge_kernel, dim3(32, batch * (a.heads / 16)), dim3(64 * kMergeWaves), 0,
-                     stream, a);
+  // About 1024 merge workgroups: value tiles per workgroup 32 / chunks.
+  const int bht = batch * (a.heads / 16);
+  int chunks = 1;
+  while (chunks < 32 && chunks * bht < 1024) chunks *= 2;
+  hipLaunchKernelGGL(decode_wide_merge_kernel, dim3(chunks, bht), dim3(64 * kMergeWaves), 0, stream, a);
   return hipGetLastError();
 }
 
