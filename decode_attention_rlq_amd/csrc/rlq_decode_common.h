@@ -267,5 +267,86 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht
   }
 }
 
+// The same merge for njp (2 .. kMergeMaxTiles) value tiles at once, for few
+// splits: wave w sums splits w, w + 4, ... of every tile in one pass (all of
+// a split's tile loads in flight together), the four sums meet in LDS once,
+// and wave w writes tiles w, w + 4, ...
+constexpr int kMergeMaxTiles = 8;
+
+__device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int b, int ht, const MergeSrc &src,
+                                  float (*wts)[16], float (*red_m)[16], float (*red_l)[16],
+                                  f4 (*part)[kMergeWaves][64]) {
+  const int S = src.S;
+  const float2 *ml = src.ml;
+  const int mls = src.ml_stride;
+  const int tid = threadIdx.x;
+  const int h = tid & 15, st = tid >> 4;
+  const int lane = tid & 63, grp = tid >> 6, hh = lane & 15;
+  const int64_t ps = src.po_stride;
+  const f4 *po = src.po + jp0 * 64 + lane;
+  {
+    float m = kNegInf;
+    for (int s = st; s < S; s += 16) m = fmaxf(m, ml[s * mls + h].x);
+    red_m[st][h] = m;
+  }
+  // The first split's tiles of this wave are loaded while the statistics are
+  // reduced.
+  f4 v[kMergeMaxTiles];
+  const int s0 = min(grp, S - 1);
+#pragma unroll
+  for (int t = 0; t < kMergeMaxTiles; ++t)
+    if (t < njp) v[t] = po[(int64_t)s0 * ps + t * 64];
+  __syncthreads();
+  {
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, red_m[i][h]);
+    const float Mc = fmaxf(M, -1e30f);  // 0 weights for empty splits
+    float l = 0.f;
+    for (int s = st; s < S; s += 16) {
+      const float2 x = ml[s * mls + h];
+      const float w = __builtin_amdgcn_exp2f(x.x - Mc);
+      wts[s][h] = w;
+      l += w * x.y;
+    }
+    red_l[st][h] = l;
+  }
+  __syncthreads();
+  f4 acc[kMergeMaxTiles];
+#pragma unroll
+  for (int t = 0; t < kMergeMaxTiles; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int s = grp; s < S; s += kMergeWaves) {
+    const float w = wts[s][hh];
+#pragma unroll
+    for (int t = 0; t < kMergeMaxTiles; ++t)
+      if (t < njp) acc[t] += w * v[t];
+    const int sn = s + kMergeWaves;
+    if (sn < S) {
+#pragma unroll
+      for (int t = 0; t < kMergeMaxTiles; ++t)
+        if (t < njp) v[t] = po[(int64_t)sn * ps + t * 64];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMergeMaxTiles; ++t)
+    if (t < njp) part[t][grp][lane] = acc[t];
+  __syncthreads();
+  float L = 0.f, Mh = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) L += red_l[i][hh];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
+  for (int t = grp; t < njp; t += kMergeWaves) {
+    const int jp = jp0 + t;
+    const f4 sum = (part[t][0][lane] + part[t][1][lane]) + (part[t][2][lane] + part[t][3][lane]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
+  }
+  if (A.lse != nullptr && jp0 == 0 && tid < 16)
+    A.lse[(int64_t)b * A.heads + ht * 16 + tid] = L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+}
+
 }  // namespace
 }  // namespace rlq

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(DecodeArgs A) {
   __shared__ float wts[kMaxSplits + 1][16];
   __shared__ float red_m[16][16], red_l[16][16];
-  __shared__ f4 part[kMergeWaves][64];
+  __shared__ f4 part[kMergeMaxTiles][kMergeWaves][64];
   const int HT = A.heads >> 4;
   const int b = blockIdx.y / HT, ht = blockIdx.y % HT;
   const int first = A.plan[2 * b], count = A.plan[2 * b + 1];
@@ -510,7 +510,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(Dec
   const MergeSrc src{(const f4 *)(A.part_o + p0 * kPartialFloats), (int64_t)HT * (kPartialFloats / 4),
                      (const float2 *)(A.part_ml + p0 * 32), HT * 16, count};
   const int njp = 32 / gridDim.x;
-  merge_tiles(A, blockIdx.x * njp, njp, b, ht, src, wts, red_m, red_l, part);
+  if (njp == 1)
+    merge_tiles(A, blockIdx.x, 1, b, ht, src, wts, red_m, red_l, part[0]);
+  else
+    merge_tiles_multi(A, blockIdx.x * njp, njp, b, ht, src, wts, red_m, red_l, part);
 }
 
 }  // namespace
@@ -553,9 +556,10 @@ hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t st
     hipLaunchKernelGGL(decode_wide_kernel<false>, grid, dim3(kDecodeThreads), kWideLds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // About 1024 merge workgroups: value tiles per workgroup 32 / chunks.
+  // About 1024 merge workgroups (at least 4 per request and head tile):
+  // value tiles per workgroup 32 / chunks, at most kMergeMaxTiles.
   const int bht = batch * (a.heads / 16);
-  int chunks = 1;
+  int chunks = 32 / kMergeMaxTiles;
   while (chunks < 32 && chunks * bht < 1024) chunks *= 2;
   hipLaunchKernelGGL(decode_wide_merge_kernel, dim3(chunks, bht), dim3(64 * kMergeWaves), 0, stream, a);
   return hipGetLastError();
