@@ -46,6 +46,7 @@ APPEND_BYTES_PER_TOKEN = 1024 + 128 + 288   # latent + RoPE key read, cache reco
 APPEND_FLOP_PER_TOKEN = 2 * 512 * 512       # z = R c
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_v2lite_256k.json")
 KERNEL_SOURCES = ["decode_attention_rlq_amd/csrc/rlq_decode.hip",
+                  "decode_attention_rlq_amd/csrc/rlq_decode_common.h",
                   "decode_attention_rlq_amd/csrc/rlq_internal.h"]
 DEFAULT_REPLICAS = {"v2lite_256k": 2, "v2lite_32k": 16, "ragged_protect": 3}
 
@@ -265,12 +266,14 @@ def bench_decode(args, torch, rlq, workloads):
     tflops = decode_flops(H, ctx) / (dec_avg * 1e-3) / 1e12
     hbm = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
            "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(args.config),
-           "kernel": "rlq_mla_decode (split-KV kernel + merge kernel)",
+           "kernel": "rlq_mla_decode (many-head kernel + merge kernel)" if H % 64 == 0 else
+                     "rlq_mla_decode (split-KV kernel + merge kernel)",
            "algorithmic_bytes_per_launch": alg_bytes, "copy_peak_gbps": copy_gbps,
            "frac_of_copy_peak": gbps / copy_gbps}
     mfma = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
-            "kernel": "rlq_mla_decode (split-KV kernel + merge kernel)",
+            "kernel": "rlq_mla_decode (many-head kernel + merge kernel)" if H % 64 == 0 else
+                      "rlq_mla_decode (split-KV kernel + merge kernel)",
             "algorithmic_flop_per_launch": decode_flops(H, ctx)}
     # 16 heads: 121 flop per byte, HBM-bound; 128 heads: 967 flop per byte, MFMA-bound.
     roofline, other = (mfma, hbm) if H >= 64 else (hbm, mfma)

@@ -185,8 +185,9 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
 /*
  * Workspace (bytes) that rlq_mla_decode needs for this batch, head count and
  * maximum context length: split-KV partials (unnormalised output, running max
- * and sum per split and head).  Errors: RLQ_EINVAL (also for max_ctx_len
- * above RLQ_MAX_CTX).
+ * and sum per split and head) and, when heads is a multiple of 64, a table of
+ * each request's work items (two int32 per request).  Errors: RLQ_EINVAL (also
+ * for max_ctx_len above RLQ_MAX_CTX).
  */
 int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
                                   size_t *bytes);
@@ -206,7 +207,9 @@ int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_
  *   q_c_bf16       device [batch][heads][512] absorbed content queries (BF16),
  *                  already in the rotated basis
  *   q_r_bf16       device [batch][heads][64] RoPE queries (BF16)
- *   heads          multiple of 16, at most 128
+ *   heads          multiple of 16, at most 128 (a multiple of 64 runs the
+ *                  many-head kernel: each token decoded once per 64 heads,
+ *                  work items balanced over ctx_lens on the device)
  *   sm_scale       softmax scale
  *   block_table    device int32 [batch][max_pages_per_req]
  *   ctx_lens       device int32 [batch], 0 <= ctx_lens[b] <= max_ctx_len
