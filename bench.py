@@ -12,6 +12,11 @@ Other workloads (each prints its own line with its own metric):
   --config ragged_protect  32 requests of log-uniform 1K..64K tokens, 128 heads,
                            4 sink + 64 recent BF16 tokens per request (MFMA-bound)
   --config append_bulk     bulk quantize-append of 4 x 65,536 new tokens
+  --config long_output     the per-step decode loop of a long generation: 4
+                           requests from 128-token prompts generate --gen-tokens
+                           tokens each (append the new token, decode over the grown
+                           cache, 4 sink + 64 recent BF16 tokens), 16 heads;
+                           reports generated tokens/s over successive intervals
 
 Prints one JSON line.  For the decode workloads `value` is context tokens per
 second of the whole step with every input already resident in HBM; `roofline`
@@ -352,13 +357,122 @@ def bench_append(args, torch, rlq, workloads):
     return res
 
 
+# --------------------------------------------------------------------------- long output
+
+LONG_OUTPUT_METRIC = "2-bit MLA long-output decode loop: generated tokens/s (4 requests, 128-token prompts)"
+
+
+def bench_long_output(args, torch, rlq, workloads):
+    """Successive-interval throughput of the generation loop.  One step =
+    quantize-append of the new token of every request (bf16 latent, MFMA
+    rotation) + decode over the cache grown by it; `unroll` steps are captured
+    in one HIP graph that also advances the device-side positions, and the
+    graph is replayed until every request has generated --gen-tokens tokens."""
+    dev = dev_of(torch)
+    B, H, prompt, gen = 4, 16, 128, args.gen_tokens
+    unroll, interval = 32, max(args.interval // 32 * 32, 32)
+    gen = (gen + interval - 1) // interval * interval
+    log(f"generating workload long_output: {B} x {prompt}-token prompts, {gen} generated tokens each")
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[prompt] * B, heads=H, n_sink=4, n_recent=64)
+    # The cache and the decode grid are sized for --gen-capacity tokens (the
+    # whole generation by default), as a server sizes them before it starts.
+    total = prompt + max(gen, args.gen_capacity)
+    ppr = (total + 63) // 64
+    perm = np.random.default_rng(7).permutation(B * ppr).astype(np.int32)
+    bt_np = perm.reshape(B, ppr)
+    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+    cache = rlq.PagedCache.allocate(B * ppr, max_batch=B, n_sink=prob.n_sink, n_recent=prob.n_recent)
+    bt, rot = dev(bt_np), dev(prob.rotation_bits)
+    rlq.quantize_append(p, cache, dev(prob.k_rope_bits), dev(prob.cu_seqlens), dev(prob.start_pos), bt,
+                        latent=dev(prob.latent_bits), rotation=rot)
+    # Step k of a replay appends the latents of prompt position k of every
+    # request again (values do not change the work); one int32 [2][B] tensor
+    # holds the append positions (row 0) and the context lengths (row 1).
+    rows = np.asarray([[int(prob.cu_seqlens[b]) + t for b in range(B)] for t in range(unroll)]).reshape(-1)
+    lat_pool = dev(prob.latent_bits[rows]).view(unroll, B, 512)
+    kr_pool = dev(prob.k_rope_bits[rows]).view(unroll, B, 64)
+    q_c, q_r = dev(prob.q_c_bits), dev(prob.q_r_bits)
+    cu_d = dev(np.arange(B + 1, dtype=np.int32))
+    pos_d = torch.tensor([[prompt] * B, [prompt + 1] * B], dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(rlq.decode_workspace_size(B, H, total), dtype=torch.uint8, device="cuda")
+
+    def step(st, k):
+        rlq.quantize_append(p, cache, kr_pool[k], cu_d, pos_d[0], bt, latent=lat_pool[k], rotation=rot,
+                            n_tokens=B, stream=st)
+        rlq.mla_decode(p, cache, q_c, q_r, prob.sm_scale, bt, pos_d[1], total, out=out, lse=lse, workspace=ws,
+                       stream=st)
+        pos_d.add_(1)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(unroll):
+            step(cap, k)
+    torch.cuda.synchronize()
+
+    def reset():
+        pos_d[0].fill_(prompt)
+        pos_d[1].fill_(prompt + 1)
+
+    log(f"warmup {args.warmup} replays of {unroll} steps")
+    reset()
+    for _ in range(max(args.warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(gen // interval + 1)]
+    log(f"timing {gen} steps ({gen // unroll} replays), events every {interval} steps")
+    ev[0].record(stream)
+    for k in range(gen // interval):
+        for _ in range(interval // unroll):
+            g.replay()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    assert int(pos_d[0, 0].item()) == prompt + gen
+    dts = [ev[k].elapsed_time(ev[k + 1]) * 1e-3 for k in range(gen // interval)]
+    t_all = sum(dts)
+    intervals = [{"context_end": prompt + (k + 1) * interval, "generated_tokens_per_s": B * interval / dt,
+                  "ms_per_step": dt * 1e3 / interval} for k, dt in enumerate(dts)]
+    ctx_sum = B * sum(prompt + t + 1 for t in range(gen))          # context tokens attended over the run
+    prot = B * sum(min(prompt + t + 1, 68) for t in range(gen))    # of which BF16 sink/recent
+    alg_bytes = (ctx_sum - prot) * BYTES_PER_TOKEN + prot * BYTES_PER_PROTECTED
+    gbps = alg_bytes / t_all / 1e9
+    log(f"{gen} steps in {t_all * 1e3:.1f} ms: {B * gen / t_all:.3g} generated tokens/s; first interval "
+        f"{intervals[0]['ms_per_step'] * 1e3:.1f} us/step, last {intervals[-1]['ms_per_step'] * 1e3:.1f} us/step")
+    return {
+        "metric": LONG_OUTPUT_METRIC, "value": B * gen / t_all, "unit": "generated tokens/s", "n_gpus": 1,
+        "steps": gen, "warmup": args.warmup, "ms_per_step": t_all * 1e3 / gen, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"long_output: {B} requests, {prompt}-token prompts, {gen} generated tokens each, "
+                               f"{H} heads, 4 sink + 64 recent BF16 tokens; one step = append 1 token per request "
+                               f"+ decode (the grid sized for the final length), {unroll} steps per HIP graph",
+                   "batch": B, "heads": H, "prompt_tokens": prompt, "generated_tokens": gen},
+        "intervals": intervals,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "whole step (append + decode), cache bytes attended per second",
+                     "algorithmic_bytes_per_run": alg_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v2lite_256k",
-                    choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk"])
+                    choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk", "long_output"])
+    ap.add_argument("--gen-tokens", type=int, default=262144,
+                    help="long_output: tokens generated per request")
+    ap.add_argument("--gen-capacity", type=int, default=0,
+                    help="long_output: size the cache and decode grid for this many generated tokens")
+    ap.add_argument("--interval", type=int, default=8192,
+                    help="long_output: steps per reported interval (a multiple of 32)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="cache copies cycled per step so no step reads a cache the MALL still holds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -388,6 +502,8 @@ def main():
     torch.cuda.set_device(0)
     if args.config == "append_bulk":
         res = bench_append(args, torch, rlq, workloads)
+    elif args.config == "long_output":
+        res = bench_long_output(args, torch, rlq, workloads)
     else:
         res = bench_decode(args, torch, rlq, workloads)
     print(json.dumps(res), flush=True)

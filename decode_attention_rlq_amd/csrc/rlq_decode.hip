@@ -87,6 +87,15 @@ __device__ inline void load_rope(const DecodeArgs &A, int64_t first, int r16, in
 }
 
 
+// Tokens per split of a request with ctx tokens: ctx spread over the launch's
+// splits in whole pages (at least 4), at most the launch's split size (which
+// covers the longest context).
+__device__ inline int split_tokens(const DecodeArgs &A, int ctx) {
+  const int per = (ctx + A.splits - 1) / A.splits;
+  const int t = max(4 * RLQ_PAGE, (per + RLQ_PAGE - 1) / RLQ_PAGE * RLQ_PAGE);
+  return min(t, A.tokens_per_split);
+}
+
 // kProt = false: the ordinary splits (partials prot .. prot + splits - 1 of a
 // request); kProt = true: the BF16 sink/recent tokens (partial 0).
 //
@@ -98,10 +107,9 @@ __device__ inline void load_rope(const DecodeArgs &A, int64_t first, int r16, in
 // waves run the same online softmax on the full scores.  The value product of
 // wave h covers latent half h, whose c_hat it wrote to its own LDS region.
 template <bool kProt>
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeArgs A) {
+__device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, const int sp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int b = blockIdx.y, hg = blockIdx.z;
-  const int sp = kProt ? -1 : (int)blockIdx.x;
   const int part = kProt ? 0 : A.prot + sp;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = wave & 1, pr = wave >> 1;  // latent half, pair
@@ -119,7 +127,29 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   }
   const bf16x8 qrB = __builtin_bit_cast(
       bf16x8, *(const u4 *)(A.q_r + ((int64_t)b * A.heads + hg * 16 + r16) * RLQ_DR + 16 * g4 + 8 * h));
+  // Page ids of the pair's tiles in one VGPR: lane l holds page
+  // p_first + (tile0 >> 1) + l (a pair's tiles span at most 64 pages), so a
+  // tile's loads need one readlane and no memory access for their page.
+  // They are fetched first for the launch's split size (right when every
+  // context is near the longest) and again below if this request's split
+  // size differs.
+  auto pid_load = [&](int tb, int ni) -> int32_t {
+    const int pf = (tb >> 6) + ((pr * ni) >> 1) + lane;
+    return (!kProt && pf < A.max_pages) ? A.block_table[(int64_t)b * A.max_pages + pf] : 0;
+  };
+  const int tps_h = A.tokens_per_split;
+  int32_t pid_pair = pid_load(sp * tps_h, (tps_h / kWaveTok + kPairs - 1) / kPairs);
   const int ctx = A.ctx_lens[b];
+  // Split size of this request: its context spread over the launch's splits
+  // (so a short request among long ones, or a grid sized for a later, longer
+  // context, still uses every split).
+  const int tps = kProt ? tps_h : split_tokens(A, ctx);
+  // A split past the context (other than split 0) has nothing to add: the
+  // merge reads only the splits that hold tokens, so it exits at once.
+  if (!kProt && sp > 0 && sp * tps >= ctx) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   const Protect pr_ = protect_range(A, ctx);
   // Token range of this workgroup: positions for ordinary splits, indices
   // into the protected list (sink positions, then recent positions) for the
@@ -129,30 +159,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
     t_begin = 0;
     t_end = pr_.ns + pr_.nr;
   } else {
-    t_begin = sp * A.tokens_per_split;
-    t_end = min(ctx, t_begin + A.tokens_per_split);
+    t_begin = sp * tps;
+    t_end = min(ctx, t_begin + tps);
   }
   const int u_lo = pr_.ns, u_hi = ctx - pr_.nr;  // unprotected positions
 
   // Tiles of the workgroup.  An ordinary split deals its nominal tile count
-  // (tokens_per_split / 32) out to the pairs, so each pair's page ids can be
-  // fetched before the context length is known; in a split cut short by the
-  // context the last pairs get fewer tiles or none.  The protected workgroup
-  // deals its tiles evenly (every pair runs n_iter steps, tiles past the end
-  // masked).
+  // (tps / 32) out to the pairs; in a split cut short by the context the last
+  // pairs get fewer tiles or none.  The protected workgroup deals its tiles
+  // evenly (every pair runs n_iter steps, tiles past the end masked).
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + kWaveTok - 1) / kWaveTok : 0;
-  const int n_iter = kProt ? (n_tiles + kPairs - 1) / kPairs
-                           : (A.tokens_per_split / kWaveTok + kPairs - 1) / kPairs;
+  const int n_iter = kProt ? (n_tiles + kPairs - 1) / kPairs : (tps / kWaveTok + kPairs - 1) / kPairs;
   const int tile0 = pr * n_iter;
   const int n_mine = min(max(n_tiles - tile0, 0), n_iter);  // ordinary splits: tiles of this pair
-  // Page ids of the pair's tiles in one VGPR: lane l holds page
-  // p_first + (tile0 >> 1) + l (a pair's tiles span at most 64 pages), so a
-  // tile's loads need one readlane and no memory access for their page.
-  const int p_first = t_begin >> 6;
   const int pp0 = tile0 >> 1;
-  const int32_t pid_pair = (!kProt && p_first + pp0 + lane < A.max_pages)
-                               ? A.block_table[(int64_t)b * A.max_pages + p_first + pp0 + lane]
-                               : 0;
+  if (!kProt && tps != tps_h) pid_pair = pid_load(t_begin, n_iter);
   const int last_mine = tile0 + n_mine - 1;
   auto tile_slot = [&](int i) -> int64_t {  // i = pair-local tile index
     // Past the pair's last tile the last one is loaded again (never
@@ -511,6 +532,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeA
   }
 }
 
+// Splits of a cache without sink/recent buffers.
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeArgs A) {
+  split_body<false>(A, (int)blockIdx.x);
+}
+
+// With sink/recent buffers, one launch holds both kinds of workgroup:
+// blockIdx.x = 0 covers the BF16 sink/recent tokens (partial 0), the others
+// the ordinary splits.
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_prot_kernel(DecodeArgs A) {
+  if (blockIdx.x == 0)
+    split_body<true>(A, -1);
+  else
+    split_body<false>(A, (int)blockIdx.x - 1);
+}
+
 // The standalone merge: 32 workgroups of 4 waves per (request, head group).
 __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs A) {
   __shared__ float wts[kMaxSplits + 1][16];
@@ -518,8 +554,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
   __shared__ f4 part[kMergeWaves][64];
   const int HG = A.heads >> 4;
   const int bh = blockIdx.y, S = A.splits + A.prot;
+  // Only the splits that hold tokens (at least split 0) were written.
+  const int ctx = A.ctx_lens[bh / HG];
+  const int tps = split_tokens(A, ctx);
+  const int used = A.prot + min(A.splits, max(1, (ctx + tps - 1) / tps));
   const MergeSrc src{(const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats), kPartialFloats / 4,
-                     (const float2 *)(A.part_ml + (int64_t)bh * S * 32), 16, S};
+                     (const float2 *)(A.part_ml + (int64_t)bh * S * 32), 16, used};
   merge_tiles(A, blockIdx.x, 1, bh / HG, bh % HG, src, wts, red_m, red_l, part);
 }
 
@@ -559,21 +599,19 @@ size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &pla
 hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    for (const void *f : {(const void *)decode_split_kernel<false>, (const void *)decode_split_kernel<true>}) {
+    for (const void *f : {(const void *)decode_split_kernel, (const void *)decode_split_prot_kernel}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return e;
     }
     attr_set = true;
   }
   const int hg = a.heads / 16;
-  if (a.prot) {
-    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(1, batch, hg), dim3(kDecodeThreads), kLdsBytes,
+  if (a.prot)
+    hipLaunchKernelGGL(decode_split_prot_kernel, dim3(a.splits + 1, batch, hg), dim3(kDecodeThreads), kLdsBytes,
                        stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid(a.splits, batch, hg);
-  hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(kDecodeThreads), kLdsBytes, stream, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel, dim3(a.splits, batch, hg), dim3(kDecodeThreads), kLdsBytes, stream,
+                       a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(32, batch * hg), dim3(64 * kMergeWaves), 0, stream, a);
