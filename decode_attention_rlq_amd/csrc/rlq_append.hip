@@ -155,8 +155,12 @@ __device__ inline void finish_group(const AppendArgs &a, const float (&z)[8][4],
     uint32_t byte = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      // code = [x >= -t] + [x >= 0] + [x >= t]; with t >= 0 (tau >= 0 is
+      // checked on the host) the sign decides which threshold still matters:
+      // x >= 0 gives 2 + [x >= t], x < 0 gives [x >= -t].
       const float x = d[mt][i];
-      const uint32_t c = (uint32_t)(x >= -t) + (uint32_t)(x >= 0.f) + (uint32_t)(x >= t);
+      const bool nonneg = x >= 0.f;
+      const uint32_t c = (nonneg ? 2u : 0u) + (uint32_t)(x >= (nonneg ? t : -t));
       byte |= c << (2 * i);
     }
     word[mt] = or_xor16_32(byte << (8 * kg));
@@ -207,6 +211,10 @@ constexpr int kBulkSlots = 8;                        // workgroups per (XCD, gro
 constexpr int kBulkGrid = 8 * RLQ_NGROUPS * kBulkSlots;  // 256: one per CU
 constexpr int kRSlice = RLQ_GROUP * 32 * 2;          // 8 KB: 128 rows x 32 K
 constexpr int kRBytes = (RLQ_DC / 32) * kRSlice;     // 128 KB
+// Request table staged in LDS after R: cu_seqlens[0..B] and start_pos[0..B-1]
+// (batches up to kLdsRequests; larger ones search global memory).
+constexpr int kLdsRequests = 2047;
+constexpr int kBulkLds = kRBytes + (2 * kLdsRequests + 2) * 4;  // 144 KB
 
 __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char rs[];
@@ -228,15 +236,50 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
       *(u4 *)(rs + chunk(kc >> 2, r, kc & 3)) =
           *(const u4 *)(a.rotation + (size_t)(G * RLQ_GROUP + r) * RLQ_DC + 8 * kc);
     }
-    __syncthreads();
   }
+  // The request table, so that finding a token's request and position needs
+  // no dependent global loads.
+  int32_t *lds_cu = (int32_t *)(rs + kRBytes);
+  int32_t *lds_start = lds_cu + kLdsRequests + 1;
+  const bool lds_table = a.batch <= kLdsRequests;
+  if (lds_table) {
+    for (int i = threadIdx.x; i <= a.batch; i += 64 * kBulkWaves) lds_cu[i] = a.cu_seqlens[i];
+    for (int i = threadIdx.x; i < a.batch; i += 64 * kBulkWaves) lds_start[i] = a.start_pos[i];
+  }
+  __syncthreads();
 
   const int64_t n_tiles = (a.n_tokens + kBulkTile - 1) / kBulkTile;
   for (int64_t tile = xcd + 8 * slot; tile < n_tiles; tile += 8 * kBulkSlots) {
     const int64_t tile0 = tile * kBulkTile + 64 * w;
-    Dest dst[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) dst[nt] = resolve(a, tile0 + nt * 16 + n);
+    // Destinations: request and position from the LDS table now, the page id
+    // load issued now and consumed after the contraction.
+    int32_t rb[4], rpg[4];
+    auto pos_of = [&](int nt) -> int32_t {
+      const int64_t tok = tile0 + nt * 16 + n;
+      const int64_t t = tok < a.n_tokens ? tok : a.n_tokens - 1;
+      return lds_start[rb[nt]] + (int32_t)(t - lds_cu[rb[nt]]);
+    };
+    auto locate = [&](int nt) {
+      const int64_t tok = tile0 + nt * 16 + n;
+      const int64_t t = tok < a.n_tokens ? tok : a.n_tokens - 1;
+      int lo = 0, hi = a.batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)lds_cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      rb[nt] = lo;
+      rpg[nt] = a.block_table[(int64_t)lo * a.max_pages + (pos_of(nt) >> 6)];
+    };
+    auto dest_of = [&](int nt) -> Dest {
+      const int64_t tok = tile0 + nt * 16 + n;
+      if (!lds_table) return resolve(a, tok);
+      const int32_t pos = pos_of(nt);
+      Dest d{-1, pos, rb[nt], 0};
+      if (tok >= a.n_tokens) return d;
+      d.slot = (int64_t)rpg[nt] * RLQ_PAGE + (pos & 63);
+      d.new_len = lds_start[rb[nt]] + (lds_cu[rb[nt] + 1] - lds_cu[rb[nt]]);
+      return d;
+    };
 
     f4 acc[4][8];
 #pragma unroll
@@ -245,6 +288,10 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
 
     if (a.latent_rot != nullptr) {
+      if (lds_table) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) locate(nt);
+      }
       // Already rotated: load z straight into the accumulator layout.
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -269,6 +316,10 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
       constexpr int kSteps = RLQ_DC / 32;
       constexpr int kCDepth = 3;
       u4 cb[kCDepth][4];
+      if (lds_table) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) locate(nt);
+      }
 #pragma unroll
       for (int k = 0; k < kCDepth; ++k)
 #pragma unroll
@@ -296,6 +347,9 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
       }
     }
 
+    Dest dst[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) dst[nt] = dest_of(nt);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float z[8][4];
@@ -394,11 +448,11 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void *)append_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRBytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kBulkLds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    hipLaunchKernelGGL(append_kernel, dim3(kBulkGrid), dim3(64 * kBulkWaves), kRBytes, stream, a);
+    hipLaunchKernelGGL(append_kernel, dim3(kBulkGrid), dim3(64 * kBulkWaves), kBulkLds, stream, a);
   }
   return hipGetLastError();
 }

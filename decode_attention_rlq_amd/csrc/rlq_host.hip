@@ -96,6 +96,7 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
                         const int32_t *block_table, int32_t max_pages_per_req,
                         int32_t batch, int64_t n_tokens, float *z_debug, void *stream) {
   if (p == nullptr || batch < 1 || n_tokens < 0 || max_pages_per_req < 1) return RLQ_EINVAL;
+  if (!(p->tau >= 0.f) || !isfinite(p->tau)) return RLQ_EINVAL;  // the code needs t = tau * s >= 0
   int st = check_cache(cache, batch);
   if (st != RLQ_OK) return st;
   if ((latent_bf16 == nullptr) == (latent_rot_f32 == nullptr)) return RLQ_EINVAL;

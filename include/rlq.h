@@ -76,7 +76,9 @@ enum {
 
 /*
  * Per-layer quantizer parameters, fixed while serving (§3.3).
- *   tau          threshold on the standardized coordinate (§3.2, §C.3)
+ *   tau          threshold on the standardized coordinate (§3.2, §C.3);
+ *                finite and >= 0 (rlq_quantize_append returns RLQ_EINVAL
+ *                otherwise)
  *   gain         reconstruction gain around the group mean (§3.2, §B.3)
  *   level_inner  a, level_outer b: the four levels are -b, -a, +a, +b
  * Defaults (rlq_layer_params_default): the four-level Lloyd-Max quantizer for

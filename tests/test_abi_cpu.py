@@ -124,6 +124,11 @@ def test_validation_rejects_before_any_launch(lib):
         assert A(ctypes.byref(p), ctypes.byref(c), None, fake, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
     assert A(ctypes.byref(p), ctypes.byref(good), None, fake, None, fake, fake, fake, fake, 1, 0, 8, None, None) == -1
     assert A(None, ctypes.byref(good), None, fake, None, fake, fake, fake, fake, 1, 1, 8, None, None) == -1
+    for bad_tau in (-0.5, float("nan"), float("inf")):  # the code assignment needs tau >= 0
+        q = rlq.default_params()
+        q.tau = bad_tau
+        assert A(ctypes.byref(q), ctypes.byref(good), None, fake, None, fake, fake, fake, fake, 1, 1, 8, None,
+                 None) == -1
     D = lib.rlq_mla_decode
     args = lambda heads, mcl, ws: (ctypes.byref(p), ctypes.byref(good), fake, fake, 1, heads, 0.1,
                                    fake, 4, fake, mcl, fake, None, fake, ws, None)

@@ -57,6 +57,10 @@ CASES = {
     # 70 requests: more than one wave's worth of cu_seqlens entries.
     "many_requests": dict(name="tiny", ctx_lens=[1 + (7 * b) % 11 for b in range(70)],
                           start=[(3 * b) % 2 for b in range(70)], n_sink=1, n_recent=3),
+    # More than 4096 new tokens: the persistent bulk kernel, with ragged
+    # requests, start offsets and protection.
+    "bulk_ragged": dict(name="tiny", ctx_lens=[1500, 3070, 7, 900, 2100], start=[0, 60, 0, 33, 64],
+                        n_sink=4, n_recent=16),
 }
 
 
