@@ -347,6 +347,16 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
       }
     }
 
+    // RoPE keys: the four group workgroups of a tile each copy one 32-byte
+    // quarter of every token's key (lane l: token tile0 + l).  The loads go
+    // out now and the stores after the statistics, which hide their latency.
+    const int64_t rtok = tile0 + lane;
+    u4 rq[2] = {};
+    if (rtok < a.n_tokens) {
+      const u4 *src = (const u4 *)(a.k_rope + rtok * RLQ_DR + 16 * G);
+      rq[0] = src[0];
+      rq[1] = src[1];
+    }
     Dest dst[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) dst[nt] = dest_of(nt);
@@ -359,8 +369,14 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
         for (int i = 0; i < 4; ++i) z[mt][i] = acc[nt][mt][i];
       finish_group(a, z, tile0 + nt * 16 + n, dst[nt], G, kg);
     }
-    // RoPE keys: group-0 workgroups, lane group kg copies N-tile kg.
-    if (G == 0) copy_rope_token(a, tile0 + kg * 16 + n, dst[kg]);
+    // Token tile0 + lane is N-tile kg, column n: its destination is dst[kg]
+    // (selected, not indexed, so dst stays in registers).
+    const int64_t rslot = kg == 0 ? dst[0].slot : kg == 1 ? dst[1].slot : kg == 2 ? dst[2].slot : dst[3].slot;
+    if (rslot >= 0) {
+      u4 *dstp = (u4 *)(a.rope + rslot * RLQ_DR + 16 * G);
+      dstp[0] = rq[0];
+      dstp[1] = rq[1];
+    }
   }
 }
 
