@@ -560,7 +560,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
   const int used = A.prot + min(A.splits, max(1, (ctx + tps - 1) / tps));
   const MergeSrc src{(const f4 *)(A.part_o + (int64_t)bh * S * kPartialFloats), kPartialFloats / 4,
                      (const float2 *)(A.part_ml + (int64_t)bh * S * 32), 16, used};
-  merge_tiles(A, blockIdx.x, 1, bh / HG, bh % HG, src, wts, red_m, red_l, part);
+  // Request bh / HG, head tile bh % HG: output rows 16 bh .. 16 bh + 15.
+  merge_tiles(A, blockIdx.x, 1, (int64_t)bh * 16, src, wts, red_m, red_l, part);
 }
 
 }  // namespace

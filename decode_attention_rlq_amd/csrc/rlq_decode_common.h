@@ -145,7 +145,9 @@ __device__ inline Protect protect_range(const DecodeArgs &A, int ctx) {
 template <bool V>
 using bool_c = std::integral_constant<bool, V>;
 
-// LSE merge of the split partials of one (request b, 16-head tile ht) for
+// LSE merge of the split partials of one 16-row tile (output rows orow ..
+// orow + 15: one request's 16-head tile, or 16 (query, head) rows of an
+// extend call) for
 // value tiles jp0 .. jp0 + njp - 1 (each 16 heads x 16 latent coordinates as
 // 64 lanes x 4) by a workgroup of four waves.  The (max, sum) statistics are
 // reduced once; then, per value tile, wave w sums splits w, w + 4, ..., and
@@ -166,7 +168,7 @@ struct MergeSrc {
   int S;
 };
 
-__device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht, const MergeSrc &src,
+__device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int64_t orow, const MergeSrc &src,
                             float (*wts)[16], float (*red_m)[16], float (*red_l)[16], f4 (*part)[64]) {
   const int S = src.S;
   const float2 *ml = src.ml;
@@ -233,7 +235,7 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht
     for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
+  float *o = A.out + (orow + hh) * RLQ_DC;
   for (int t = 0; t < njp; ++t) {
     const int jp = jp0 + t;
     const f4 *po = src.po + jp * 64 + lane;
@@ -260,7 +262,7 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
       if (A.lse != nullptr && jp == 0 && lane < 16)
-        A.lse[(int64_t)b * A.heads + ht * 16 + lane] =
+        A.lse[orow + lane] =
             L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
     }
     if (t + 1 < njp) __syncthreads();  // part is rewritten by the next tile
@@ -273,7 +275,7 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int b, int ht
 // and wave w writes tiles w, w + 4, ...
 constexpr int kMergeMaxTiles = 8;
 
-__device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int b, int ht, const MergeSrc &src,
+__device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int64_t orow, const MergeSrc &src,
                                   float (*wts)[16], float (*red_m)[16], float (*red_l)[16],
                                   f4 (*part)[kMergeWaves][64]) {
   const int S = src.S;
@@ -337,7 +339,7 @@ __device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int b, 
 #pragma unroll
   for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float *o = A.out + ((int64_t)b * A.heads + ht * 16 + hh) * RLQ_DC;
+  float *o = A.out + (orow + hh) * RLQ_DC;
   for (int t = grp; t < njp; t += kMergeWaves) {
     const int jp = jp0 + t;
     const f4 sum = (part[t][0][lane] + part[t][1][lane]) + (part[t][2][lane] + part[t][3][lane]);
@@ -345,7 +347,7 @@ __device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int b, 
     for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
   }
   if (A.lse != nullptr && jp0 == 0 && tid < 16)
-    A.lse[(int64_t)b * A.heads + ht * 16 + tid] = L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+    A.lse[orow + tid] = L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace

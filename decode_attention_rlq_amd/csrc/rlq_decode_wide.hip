@@ -60,6 +60,27 @@ __device__ inline int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
+// Query rows of request b: first row (in q_c / q_r / out / lse, in rows of
+// 512 / 64 / 512 / 1 elements), row count and query count.
+struct QueryRows {
+  int64_t row0;
+  int n_rows, n_q;
+};
+__device__ inline QueryRows query_rows(const DecodeArgs &A, int b) {
+  QueryRows r;
+  if (A.cu_q != nullptr) {
+    const int q0 = A.cu_q[b];
+    r.n_q = A.cu_q[b + 1] - q0;
+    r.row0 = (int64_t)q0 * A.q_heads;
+    r.n_rows = r.n_q * A.q_heads;
+  } else {
+    r.n_q = 1;
+    r.row0 = (int64_t)b * A.heads;
+    r.n_rows = A.heads;
+  }
+  return r;
+}
+
 struct Item {
   int b;       // request
   int tb, te;  // tiles [tb, te) of the request (tile t = positions 32t .. 32t+31)
@@ -165,16 +186,20 @@ __device__ inline int rope_off(int t, int c) { return t * 128 + 16 * (c ^ ((t >>
 template <bool kProt>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int x = blockIdx.x, hq = blockIdx.y;  // work item, 64-head group
+  const int x = blockIdx.x, hq = blockIdx.y;  // work item, 64-row group
   Item it;
   if (!find_item(A, x, it)) return;
   const int b = it.b;
+  const int head0 = kWideHeads * hq;
+  // Query rows of the request: its heads (decode), or (query, head) rows
+  // (extend: query i at position ctx - n_q + i sees positions 0 .. ctx - n_q + i).
+  const QueryRows qr = query_rows(A, b);
+  if (head0 >= qr.n_rows) return;  // every row of this group is past the request's last
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = wave & 1, pr = wave >> 1;  // latent half, pair = head tile
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int HT = A.heads >> 4;
-  const int head0 = kWideHeads * hq;
 
   // ---- absorbed query of 64 heads, converted to fp16 and scattered through
   // LDS into operand order (row = head hd, K-step k, lane group g, slot j at
@@ -182,13 +207,25 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   constexpr int kQChunks = kWideHeads * RLQ_DC / 8 / kDecodeThreads;  // 8 per thread
   u4 qv[kQChunks];
   {
-    const uint16_t *qsrc = A.q_c + ((int64_t)b * A.heads + head0) * RLQ_DC;
+    // Rows past the request's last one read its last row (never used).
 #pragma unroll
-    for (int j = 0; j < kQChunks; ++j) qv[j] = *(const u4 *)(qsrc + 8 * (threadIdx.x + j * kDecodeThreads));
+    for (int j = 0; j < kQChunks; ++j) {
+      const int c = threadIdx.x + j * kDecodeThreads;
+      const int row = min(head0 + (c >> 6), qr.n_rows - 1);
+      qv[j] = *(const u4 *)(A.q_c + (qr.row0 + row) * RLQ_DC + 8 * (c & 63));
+    }
   }
-  const bf16x8 qrB = __builtin_bit_cast(
-      bf16x8, *(const u4 *)(A.q_r + ((int64_t)b * A.heads + head0 + 16 * pr + r16) * RLQ_DR + 16 * g4 + 8 * h));
+  const int qrow = min(head0 + 16 * pr + r16, qr.n_rows - 1);
+  const bf16x8 qrB =
+      __builtin_bit_cast(bf16x8, *(const u4 *)(A.q_r + (qr.row0 + qrow) * RLQ_DR + 16 * g4 + 8 * h));
   const int ctx = min(A.ctx_lens[b], A.max_ctx_len);
+  // Positions this pair's rows attend to: [0, lim).  A head tile never spans
+  // two queries (heads is a multiple of 16); tiles past the last row see none.
+  int lim = ctx;
+  if (A.cu_q != nullptr) {
+    const int row_t = head0 + 16 * pr;
+    lim = row_t < qr.n_rows ? ctx - qr.n_q + row_t / A.q_heads + 1 : 0;
+  }
   const Protect pt = protect_range(A, ctx);
   const int n = it.te - it.tb;  // tiles of this item
   const int pg0 = it.tb >> 1;   // first page (in the request's block table)
@@ -316,14 +353,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     sc[0] = h == 0 ? acc_prev[0] + o0 : o0 + acc_prev[0];
     sc[1] = h == 0 ? acc_prev[1] + o1 : o1 + acc_prev[1];
     // sc[st][j] = raw score of position c0 + 16*st + 4*g4 + j, head r16.
-    // Positions past the context score -inf.
-    if (c0 + kWaveTok > ctx) {
+    // Positions past the context (or, for extend, past the query) score -inf.
+    if (c0 + kWaveTok > lim) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = c0 + 16 * st + 4 * g4 + j;
-          sc[st][j] = t < ctx ? sc[st][j] : kNegInf;
+          sc[st][j] = t < lim ? sc[st][j] : kNegInf;
         }
     }
     half2v ph[4];
@@ -505,15 +542,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(Dec
   __shared__ f4 part[kMergeMaxTiles][kMergeWaves][64];
   const int HT = A.heads >> 4;
   const int b = blockIdx.y / HT, ht = blockIdx.y % HT;
+  const QueryRows qr = query_rows(A, b);
+  if (16 * ht >= qr.n_rows) return;  // no such rows in this request
   const int first = A.plan[2 * b], count = A.plan[2 * b + 1];
   const int64_t p0 = (int64_t)first * HT + ht;
   const MergeSrc src{(const f4 *)(A.part_o + p0 * kPartialFloats), (int64_t)HT * (kPartialFloats / 4),
                      (const float2 *)(A.part_ml + p0 * 32), HT * 16, count};
   const int njp = 32 / gridDim.x;
+  const int64_t orow = qr.row0 + 16 * ht;
   if (njp == 1)
-    merge_tiles(A, blockIdx.x, 1, b, ht, src, wts, red_m, red_l, part[0]);
+    merge_tiles(A, blockIdx.x, 1, orow, src, wts, red_m, red_l, part[0]);
   else
-    merge_tiles_multi(A, blockIdx.x * njp, njp, b, ht, src, wts, red_m, red_l, part);
+    merge_tiles_multi(A, blockIdx.x * njp, njp, orow, src, wts, red_m, red_l, part);
 }
 
 }  // namespace
@@ -533,6 +573,10 @@ WidePlan plan_wide(int32_t batch, int32_t heads, int32_t max_ctx_len) {
   slots = (slots + 7) / 8 * 8;
   p.item_slots = (int32_t)slots;
   return p;
+}
+
+int64_t extend_rows(int32_t max_q_len, int32_t heads) {
+  return ((int64_t)max_q_len * heads + kWideHeads - 1) / kWideHeads * kWideHeads;
 }
 
 size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan) {

@@ -203,6 +203,8 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   a.max_ctx_len = max_ctx_len;
   a.item_slots = wplan.item_slots;
   a.item_target = wplan.item_target;
+  a.cu_q = nullptr;
+  a.q_heads = heads;
   if (wide) {
     // Many heads: balanced work items, each 32-token tile decoded once per 64 heads.
     const size_t parts = (size_t)wplan.item_slots * (heads / 16);
@@ -216,6 +218,87 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   a.part_ml = a.part_o + parts * rlq::kPartialFloats;
   a.plan = nullptr;
   return hip_status(rlq::launch_decode(a, batch, (hipStream_t)stream));
+}
+
+// Extend: the many-head kernel over (query, head) rows, the rows of the
+// largest request padded to a multiple of 64.
+static bool extend_shape(int32_t batch, int32_t heads, int32_t max_q_len, int32_t max_ctx_len,
+                         int64_t *rows) {
+  if (batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16 || max_q_len < 1 ||
+      max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX || max_q_len > max_ctx_len)
+    return false;
+  *rows = rlq::extend_rows(max_q_len, heads);
+  return *rows / 64 <= 65535 && (int64_t)batch * (*rows / 16) <= 65535;
+}
+
+int rlq_mla_extend_workspace_size(int32_t batch, int32_t heads, int32_t max_q_len,
+                                  int32_t max_ctx_len, size_t *bytes) {
+  int64_t rows;
+  if (bytes == nullptr || !extend_shape(batch, heads, max_q_len, max_ctx_len, &rows)) return RLQ_EINVAL;
+  *bytes = rlq::wide_workspace_bytes(batch, (int32_t)rows, rlq::plan_wide(batch, (int32_t)rows, max_ctx_len));
+  return RLQ_OK;
+}
+
+int rlq_mla_extend(const rlq_layer_params *p, const rlq_cache *cache,
+                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                   const int32_t *cu_seqlens_q, int32_t batch, int32_t heads,
+                   int32_t max_q_len, float sm_scale,
+                   const int32_t *block_table, int32_t max_pages_per_req,
+                   const int32_t *ctx_lens, int32_t max_ctx_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  int64_t rows;
+  if (p == nullptr || !extend_shape(batch, heads, max_q_len, max_ctx_len, &rows)) return RLQ_EINVAL;
+  if (max_pages_per_req < 1 || (int64_t)max_ctx_len > (int64_t)max_pages_per_req * RLQ_PAGE)
+    return RLQ_EINVAL;
+  int st = check_cache(cache, batch);
+  if (st != RLQ_OK) return st;
+  if (q_c_bf16 == nullptr || q_r_bf16 == nullptr || cu_seqlens_q == nullptr || block_table == nullptr ||
+      ctx_lens == nullptr || out == nullptr || workspace == nullptr)
+    return RLQ_EINVAL;
+  if (!aligned(q_c_bf16, 16) || !aligned(q_r_bf16, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
+      !aligned(cu_seqlens_q, 4) || (lse != nullptr && !aligned(lse, 4)))
+    return RLQ_EINVAL;
+  const rlq::WidePlan wplan = rlq::plan_wide(batch, (int32_t)rows, max_ctx_len);
+  if (workspace_bytes < rlq::wide_workspace_bytes(batch, (int32_t)rows, wplan)) return RLQ_ENOSPC;
+  st = check_device();
+  if (st != RLQ_OK) return st;
+
+  rlq::DecodeArgs a;
+  a.codes = cache->codes;
+  a.meta = cache->meta;
+  a.rope = cache->rope;
+  a.sink = cache->sink;
+  a.recent = cache->recent;
+  a.n_sink = cache->sink ? cache->n_sink : 0;
+  a.n_recent = cache->recent ? cache->n_recent : 0;
+  a.q_c = q_c_bf16;
+  a.q_r = q_r_bf16;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_req;
+  a.ctx_lens = ctx_lens;
+  a.heads = (int32_t)rows;
+  a.tokens_per_split = 0;
+  a.splits = 0;
+  a.prot = ((a.sink != nullptr && a.n_sink > 0) || (a.recent != nullptr && a.n_recent > 0)) ? 1 : 0;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.gain = p->gain;
+  a.level_inner = p->level_inner;
+  a.level_outer = p->level_outer;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.max_ctx_len = max_ctx_len;
+  a.item_slots = wplan.item_slots;
+  a.item_target = wplan.item_target;
+  a.cu_q = cu_seqlens_q;
+  a.q_heads = heads;
+  const size_t parts = (size_t)wplan.item_slots * (size_t)(rows / 16);
+  a.part_o = (float *)workspace;
+  a.part_ml = a.part_o + parts * rlq::kPartialFloats;
+  a.plan = (int32_t *)(a.part_ml + parts * 32);
+  return hip_status(rlq::launch_decode_wide(a, batch, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -88,6 +88,12 @@ struct DecodeArgs {
   int32_t item_slots;   // workgroups per 64-head group: work items at most
   int32_t item_target;  // work items the balanced plan aims for
   int32_t *plan;        // [B][2]: first work item and item count of each request
+  // Extend (many query tokens per request): null for decode.  Request b's
+  // query rows are (query i, head h) for i < cu_q[b+1] - cu_q[b], stored from
+  // row cu_q[b] * q_heads; `heads` is then the padded row count of the
+  // largest request (a multiple of 64).
+  const int32_t *cu_q;
+  int32_t q_heads;
 };
 
 // Split policy shared by the workspace query and the launch.
@@ -118,5 +124,9 @@ struct WidePlan {
 WidePlan plan_wide(int32_t batch, int32_t heads, int32_t max_ctx_len);
 size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan);
 hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t stream);
+
+// Extend: the many-head kernel over (query, head) rows.  Padded row count of
+// the largest request, and the grid limits it must respect.
+int64_t extend_rows(int32_t max_q_len, int32_t heads);
 
 }  // namespace rlq

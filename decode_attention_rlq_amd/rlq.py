@@ -22,6 +22,7 @@ DC, DR, GROUP, NGROUPS, PAGE, WORDS = 512, 64, 128, 4, 64, 32
 EXPORTED = (
     "rlq_abi_version", "rlq_layer_params_default", "rlq_status_string", "rlq_last_hip_error",
     "rlq_coupled_gain", "rlq_quantize_append", "rlq_mla_decode_workspace_size", "rlq_mla_decode",
+    "rlq_mla_extend_workspace_size", "rlq_mla_extend",
 )
 
 
@@ -70,6 +71,12 @@ def lib() -> ctypes.CDLL:
     L.rlq_mla_decode.restype = ctypes.c_int
     L.rlq_mla_decode.argtypes = [
         ctypes.POINTER(LayerParams), ctypes.POINTER(CacheDesc), vp, vp, i32, i32, f32,
+        vp, i32, vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    L.rlq_mla_extend_workspace_size.restype = ctypes.c_int
+    L.rlq_mla_extend_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.rlq_mla_extend.restype = ctypes.c_int
+    L.rlq_mla_extend.argtypes = [
+        ctypes.POINTER(LayerParams), ctypes.POINTER(CacheDesc), vp, vp, vp, i32, i32, i32, f32,
         vp, i32, vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
     _lib = L
     return L
@@ -211,4 +218,39 @@ def mla_decode(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "rlq_mla_decode")
+    return out, lse
+
+
+def extend_workspace_size(batch: int, heads: int, max_q_len: int, max_ctx_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().rlq_mla_extend_workspace_size(batch, heads, max_q_len, max_ctx_len, ctypes.byref(n)),
+           "rlq_mla_extend_workspace_size")
+    return n.value
+
+
+def mla_extend(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.Tensor,
+               cu_seqlens_q: torch.Tensor, max_q_len: int, sm_scale: float, block_table: torch.Tensor,
+               ctx_lens: torch.Tensor, max_ctx_len: int, *, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, want_lse: bool = True,
+               workspace: torch.Tensor | None = None, stream=None):
+    """rlq_mla_extend (see include/rlq.h): q_c [total_q][heads][512].  Returns (out, lse)."""
+    total_q, heads = q_c.shape[0], q_c.shape[1]
+    batch = cu_seqlens_q.shape[0] - 1
+    if out is None:
+        out = torch.empty((total_q, heads, DC), dtype=torch.float32, device=q_c.device)
+    if lse is None and want_lse:
+        lse = torch.empty((total_q, heads), dtype=torch.float32, device=q_c.device)
+    need = extend_workspace_size(batch, heads, max_q_len, max_ctx_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_c.device)
+    desc = cache.desc()
+    st = lib().rlq_mla_extend(
+        ctypes.byref(p), ctypes.byref(desc), _ptr(q_c, torch.bfloat16, "q_c"),
+        _ptr(q_r, torch.bfloat16, "q_r"), _ptr(cu_seqlens_q, torch.int32, "cu_seqlens_q"), batch, heads,
+        int(max_q_len), float(sm_scale), _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), int(max_ctx_len),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "rlq_mla_extend")
     return out, lse

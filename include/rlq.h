@@ -233,6 +233,57 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
                    float *out, float *lse,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Workspace (bytes) that rlq_mla_extend needs: split partials for
+ * (query, head) rows, max_q_len * heads rows rounded up to 64 per request,
+ * and the work-item table.  Errors: RLQ_EINVAL (heads, batch, max_q_len < 1,
+ * max_ctx_len above RLQ_MAX_CTX, or a row count beyond the launch limits:
+ * batch * rows / 16 and rows / 64 at most 65535).
+ */
+int rlq_mla_extend_workspace_size(int32_t batch, int32_t heads, int32_t max_q_len,
+                                  int32_t max_ctx_len, size_t *bytes);
+
+/*
+ * rlq_mla_extend - prefill / extend attention of many new query tokens per
+ * request over the cache ([RoLaQ] §D: the method serves prefill and decode
+ * with kernels that read its cache; the attention itself is that of
+ * rlq_mla_decode, §2.1, §3.2, §3.3).
+ *
+ * The new tokens are appended first (rlq_quantize_append), so request b's
+ * cache holds ctx_lens[b] tokens and its n_q = cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] queries are its last n_q positions: query i sits at
+ * position p = ctx_lens[b] - n_q + i and attends causally to positions
+ * 0 .. p, each read exactly as rlq_mla_decode reads it (sink and recent BF16
+ * rows as the cache holds them after the append, i.e. the recent window is
+ * the last n_recent positions of ctx_lens[b]).  For query row r = cu_q[b] + i
+ * and head h:
+ *   out[r][h] = sum_{t <= p} softmax(s)_t c_hat_t,   lse[r][h] = ln sum exp(s_t)
+ * with s_t as in rlq_mla_decode.  n_q = 1 is the decode of the last token.
+ *
+ *   q_c_bf16       device [total_q][heads][512] absorbed content queries,
+ *                  total_q = cu_seqlens_q[batch]
+ *   q_r_bf16       device [total_q][heads][64] RoPE queries
+ *   cu_seqlens_q   device int32 [batch+1], cu_seqlens_q[0] = 0, with
+ *                  0 <= n_q <= min(ctx_lens[b], max_q_len) per request
+ *   heads          multiple of 16, at most 128
+ *   max_q_len      host bound on n_q (sizes the grid)
+ *   block_table, ctx_lens, max_ctx_len, sm_scale   as in rlq_mla_decode
+ *   out            device fp32 [total_q][heads][512]
+ *   lse            device fp32 [total_q][heads], or NULL
+ *   workspace      device scratch of rlq_mla_extend_workspace_size() bytes
+ * Device-resident counts are trusted (as for decode): n_q above max_q_len or
+ * ctx_lens[b] is undefined behaviour.
+ * Errors: RLQ_EINVAL, RLQ_ENOSPC, RLQ_EUNSUPPORTED, RLQ_EHIP.
+ */
+int rlq_mla_extend(const rlq_layer_params *p, const rlq_cache *cache,
+                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                   const int32_t *cu_seqlens_q, int32_t batch, int32_t heads,
+                   int32_t max_q_len, float sm_scale,
+                   const int32_t *block_table, int32_t max_pages_per_req,
+                   const int32_t *ctx_lens, int32_t max_ctx_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,11 @@ Pins (tests/test_oracle_*.py) and which functions they cover:
   decode                -> T=1, q=0, T=2 closed forms, permutation invariance,
                            mpmath brute force, library softmax attention in the
                            all-protected case.
+  extend                -> one query equals decode; without protection query i
+                           equals decode over its first p+1 positions; q=0
+                           gives the mean of the visible rows (protected rows
+                           substituted as the cache holds them) and lse
+                           ln(p+1); mpmath brute force of a causal tiny case.
   lse_merge             -> merge of disjoint ranges equals the whole.
 No function is "parity unpinned".
 """
@@ -479,6 +484,43 @@ def decode(cache: Cache, q_c_bf16: np.ndarray, q_r_bf16: np.ndarray, sm_scale: f
         c_hat, k_r = gather_request(cache, bt[b], n, gain, level_inner, level_outer)
         c_hat = _protected_rows(cache, b, n, c_hat)
         out[b], lse[b] = attend(qc[b], qr[b], c_hat, k_r, sm_scale)
+    return out, lse
+
+
+def extend(cache: Cache, q_c_bf16: np.ndarray, q_r_bf16: np.ndarray, sm_scale: float,
+           block_table, ctx_lens, cu_seqlens_q, gain: float, level_inner: float,
+           level_outer: float):
+    """Prefill / extend attention of each request's newest tokens over the cache.
+
+    [RoLaQ] §D: the method serves prefill as well as decode from its cache;
+    the attention is the decode attention of §2.1 / §3.3 with the causal
+    limit of a prefill.  Reading taken: the new tokens are already appended,
+    so request b holds ctx_lens[b] positions and its n_q = cu[b+1] - cu[b]
+    queries are the last n_q of them; query i (row cu[b] + i of q_c [N_q][H]
+    [d_c]) sits at position p = ctx_lens[b] - n_q + i and attends to positions
+    0 .. p, each reconstructed exactly as decode reconstructs it with the cache
+    state at ctx_lens[b] (sink rows, the recent ring of the last n_recent
+    positions, codes elsewhere).
+    Returns (out fp64 [N_q][H][d_c], lse fp64 [N_q][H]).
+    """
+    qc = bf16_bits_to_f64(q_c_bf16)
+    qr = bf16_bits_to_f64(q_r_bf16)
+    n_total, h, d_c = qc.shape
+    out = np.zeros((n_total, h, d_c))
+    lse = np.full((n_total, h), -np.inf)
+    bt = np.asarray(block_table)
+    cu = np.asarray(cu_seqlens_q)
+    for b in range(len(cu) - 1):
+        n = int(ctx_lens[b])
+        n_q = int(cu[b + 1] - cu[b])
+        if n_q == 0:
+            continue
+        c_hat, k_r = gather_request(cache, bt[b], n, gain, level_inner, level_outer)
+        c_hat = _protected_rows(cache, b, n, c_hat)
+        for i in range(n_q):
+            p = n - n_q + i
+            r = int(cu[b]) + i
+            out[r], lse[r] = attend(qc[r], qr[r], c_hat[:p + 1], k_r[:p + 1], sm_scale)
     return out, lse
 
 

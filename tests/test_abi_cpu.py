@@ -136,3 +136,30 @@ def test_validation_rejects_before_any_launch(lib):
     assert D(*args(256, 64, 1 << 30)) == -1     # too many heads
     assert D(*args(16, 257, 1 << 30)) == -1     # context beyond the block table
     assert D(*args(16, 256, 16)) == -3          # workspace too small
+
+
+def test_extend_workspace_and_validation(lib):
+    """rlq_mla_extend: (query, head) rows per request padded to 64, partials
+    per item slot and 16-row tile; validation fails before any launch."""
+    per = (16 * 512 + 32) * 4
+    for batch, heads, max_q, ctx in [(4, 16, 512, 33280), (2, 128, 7, 1000), (3, 16, 1, 64)]:
+        size = rlq.extend_workspace_size(batch, heads, max_q, ctx)
+        rows = -(-max_q * heads // 64) * 64
+        parts, rem = divmod(size - 8 * batch, per)
+        assert rem == 0 and parts % (rows // 16) == 0 and (parts // (rows // 16)) % 8 == 0
+    for bad in [(1, 24, 4, 100), (0, 16, 4, 100), (1, 16, 0, 100), (1, 16, 101, 100), (1, 144, 4, 100),
+                (64, 128, 1024, 2048)]:  # the last exceeds the launch grid
+        with pytest.raises(ValueError):
+            rlq.extend_workspace_size(*bad)
+    p = rlq.default_params()
+    fake = ctypes.c_void_p(0x100000)
+    good = rlq.CacheDesc(0x100000, 0x100000, 0x100000, 4, 64, None, None, 0, 0, 0)
+    E = lib.rlq_mla_extend
+    args = lambda cuq, heads, mq, mcl, ws: (ctypes.byref(p), ctypes.byref(good), fake, fake, cuq, 1, heads, mq, 0.1,
+                                            fake, 4, fake, mcl, fake, None, fake, ws, None)
+    assert E(*args(None, 16, 4, 64, 1 << 30)) == -1   # no cu_seqlens_q
+    assert E(*args(fake, 8, 4, 64, 1 << 30)) == -1    # heads not a multiple of 16
+    assert E(*args(fake, 16, 0, 64, 1 << 30)) == -1   # no queries
+    assert E(*args(fake, 16, 65, 64, 1 << 30)) == -1  # more queries than context
+    assert E(*args(fake, 16, 4, 257, 1 << 30)) == -1  # context beyond the block table
+    assert E(*args(fake, 16, 4, 64, 16)) == -3        # workspace too small
