@@ -12,6 +12,9 @@ Other workloads (each prints its own line with its own metric):
   --config ragged_protect  32 requests of log-uniform 1K..64K tokens, 128 heads,
                            4 sink + 64 recent BF16 tokens per request (MFMA-bound)
   --config append_bulk     bulk quantize-append of 4 x 65,536 new tokens
+  --config extend_32k      prefill / extend attention of a 512-token chunk per
+                           request over 4 x 32,768 cached tokens (the chunk's own
+                           positions included, causal), 16 heads (MFMA-bound)
   --config long_output     the per-step decode loop of a long generation: 4
                            requests from 128-token prompts generate --gen-tokens
                            tokens each (append the new token, decode over the grown
@@ -460,13 +463,119 @@ def bench_long_output(args, torch, rlq, workloads):
     }
 
 
+# --------------------------------------------------------------------------- extend (prefill chunk)
+
+def extend_flops(heads, ctx, n_q):
+    """2 (576 + 512) flop per (query, visible position, head): query i of a
+    request with ctx positions and n_q queries sees ctx - n_q + i + 1."""
+    vis = sum(int(c) * n - n * (n - 1) // 2 for c, n in zip(ctx, n_q))
+    return 2.0 * (RLQ_DC_R + 512) * heads * vis
+
+
+RLQ_DC_R = 576  # score contraction: 512 latent + 64 RoPE
+
+
+def cpu_baseline_extend(prob, oc_builder, qc, qr, cuq, n_sample):
+    """The oracle's extend for the first n_sample queries of request 0."""
+    import oracle
+    log("cpu baseline: oracle setup (quantize request 0's cache)")
+    oc, ctx0 = oc_builder()
+    n = min(n_sample, int(cuq[1]))
+    nq0 = int(cuq[1])
+    # Queries 0 .. n-1 of request 0 (positions ctx0 - nq0 .. ctx0 - nq0 + n - 1).
+    log(f"cpu baseline: timed oracle extend of {n} queries")
+    t0 = time.perf_counter()
+    sub_ctx = ctx0 - nq0 + n  # the same positions as the first n queries of the chunk
+    oracle.extend(oc, qc[:n], qr[:n], prob.sm_scale, prob.block_table[:1], [sub_ctx], [0, n],
+                  prob.gain, prob.level_inner, prob.level_outer)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "query tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"fp64 extend of the first {n} of {nq0} chunk queries of one request "
+                      f"({ctx0} cached tokens, {prob.heads} heads): {dt:.2f} s"}
+
+
+def bench_extend(args, torch, rlq, workloads):
+    dev = dev_of(torch)
+    log("generating workload extend_32k (cache of v2lite_32k)")
+    prob = workloads.make_problem("v2lite_32k")
+    B, H = prob.batch, prob.heads
+    ctx = prob.ctx_lens.astype(np.int32)
+    chunk = min(args.chunk, int(ctx.min()))
+    n_q = [chunk] * B
+    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+    c = rlq.PagedCache.allocate(prob.num_pages, max_batch=B)
+    bt, ctx_d = dev(prob.block_table), dev(ctx)
+    log(f"prefill: quantize-append {prob.n_tokens} tokens")
+    rlq.quantize_append(p, c, dev(prob.k_rope_bits), dev(prob.cu_seqlens), dev(prob.start_pos), bt,
+                        latent=dev(prob.latent_bits), rotation=dev(prob.rotation_bits))
+    rng = np.random.default_rng(7)
+    total = chunk * B
+    qc = workloads.to_bf16_bits(rng.standard_normal((total, H, 512), dtype=np.float32))
+    qr = workloads.to_bf16_bits(rng.standard_normal((total, H, 64), dtype=np.float32))
+    cuq = np.arange(0, total + 1, chunk, dtype=np.int32)
+    q_c, q_r, cuq_d = dev(qc), dev(qr), dev(cuq)
+    max_ctx = int(ctx.max())
+    out = torch.empty((total, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((total, H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(rlq.extend_workspace_size(B, H, chunk, max_ctx), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        rlq.mla_extend(p, c, q_c, q_r, cuq_d, chunk, prob.sm_scale, bt, ctx_d, max_ctx, out=out, lse=lse,
+                       workspace=ws, stream=stream)
+
+    log(f"warmup {args.warmup} calls")
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 5)
+    log(f"timing {steps} calls")
+    ms, chunks = timed_loop(torch, stream, call, steps, chunks=min(5, steps))
+    log(f"extend call {ms * 1e3:.1f} us (chunk means {min(chunks) * 1e3:.1f} .. {max(chunks) * 1e3:.1f})")
+    flops = extend_flops(H, ctx, n_q)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # Cache once, queries in, outputs and LSE out.
+    cache_bytes = int(ctx.sum()) * BYTES_PER_TOKEN + total * H * ((512 + 64) * 2 + 512 * 4 + 4)
+    gbps = cache_bytes / (ms * 1e-3) / 1e9
+    workload = (f"extend_32k: prefill chunk of {chunk} new tokens per request attending causally to "
+                f"{B} x {max_ctx} cached tokens (chunk included), {H} heads, latent 512 + RoPE 64, "
+                f"2-bit codes, group 128, page 64")
+    res = {
+        "metric": "2-bit MLA extend (prefill chunk) query tokens/s and MFMA TFLOP/s (% peak)",
+        "value": total / (ms * 1e-3), "unit": "query tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": workload, "batch": B, "chunk": chunk, "context_tokens": int(ctx.sum()), "heads": H},
+        "extend_us": ms * 1e3, "extend_spread": spread(chunks),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "rlq_mla_extend (many-head kernel over (query, head) rows + merge kernel)",
+                     "algorithmic_flop_per_launch": flops,
+                     "other_bound": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": gbps / HBM_PEAK_GBPS}},
+    }
+    if not args.no_cpu_baseline:
+        def build_request0():
+            import oracle
+            oc = oracle.new_cache(prob.num_pages)
+            n0 = int(prob.cu_seqlens[1])
+            oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[:n0], np.array([0, n0], np.int32),
+                                   np.zeros(1, np.int32), prob.block_table[:1],
+                                   latent_bf16=prob.latent_bits[:n0], rotation_bf16=prob.rotation_bits)
+            return oc, n0
+        res["cpu_baseline"] = cpu_baseline_extend(prob, build_request0, qc, qr, cuq, chunk)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v2lite_256k",
-                    choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk", "long_output"])
+                    choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk", "long_output",
+                             "extend_32k"])
+    ap.add_argument("--chunk", type=int, default=512, help="extend_32k: new (query) tokens per request")
     ap.add_argument("--gen-tokens", type=int, default=262144,
                     help="long_output: tokens generated per request")
     ap.add_argument("--gen-capacity", type=int, default=0,
@@ -504,6 +613,8 @@ def main():
         res = bench_append(args, torch, rlq, workloads)
     elif args.config == "long_output":
         res = bench_long_output(args, torch, rlq, workloads)
+    elif args.config == "extend_32k":
+        res = bench_extend(args, torch, rlq, workloads)
     else:
         res = bench_decode(args, torch, rlq, workloads)
     print(json.dumps(res), flush=True)

@@ -561,9 +561,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(Dec
 WidePlan plan_wide(int32_t batch, int32_t heads, int32_t max_ctx_len) {
   WidePlan p;
   // One round of workgroups that fills the GPU: one per CU, two per item
-  // for 128 heads.
+  // for 128 heads.  At least one item per XCD: the row groups of an item
+  // share its XCD, so with many row groups (extend) and fewer than 8 items
+  // some XCDs would get no work.
   const int hq = heads >= kWideHeads ? heads / kWideHeads : 1;
-  p.item_target = kResidentWide / hq;
+  p.item_target = kResidentWide / hq > 8 ? kResidentWide / hq : 8;
   const int64_t max_tiles = ((int64_t)max_ctx_len + kWaveTok - 1) / kWaveTok;
   const int64_t per_req = max_tiles > 0 ? (max_tiles + kMaxItemTiles - 1) / kMaxItemTiles : 1;
   int64_t slots = (int64_t)batch * per_req;
