@@ -228,6 +228,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   __syncthreads();
 
   float m_run = kNegInf, l_run = 0.f;
+  const float pinf = opaque_inf();
   f4 O[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) O[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -277,7 +278,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     auto exps = [&]() {
       // While no finite score has been seen the clamp keeps the exponent
       // finite (exp2(-inf) = 0, never NaN).
-      const float mb = fmaxf(m_run, -1e30f) - kBias;
+      const float mb = max_nn(m_run, -1e30f, pinf) - kBias;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         ph[2 * st] = __builtin_convertvector(
@@ -294,9 +295,9 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     // reduction off the critical path.  When the tile exceeds the running max
     // by more than kLazy the max moves, O is rescaled and P recomputed.
     exps();
-    float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mt = max_over_groups(mt) * A.scale_log2;
+    auto mx = [&](float x, float y) { return max_nn(x, y, pinf); };
+    float mt = mx(mx(mx(sc[0][0], sc[0][1]), mx(sc[0][2], sc[0][3])), mx(mx(sc[1][0], sc[1][1]), mx(sc[1][2], sc[1][3])));
+    mt = max_over_groups(mt, pinf) * A.scale_log2;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);

@@ -67,12 +67,23 @@ __device__ inline uint32_t h16(float x) {
 }
 __device__ inline float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
+// max(x, y) of scores, which are finite or -inf (never NaN): one v_med3 with
+// +inf (med3(x, y, +inf) = max(x, y)).  The +inf goes through an empty asm so
+// the compiler cannot fold the med3 into maxnum, which it would precede with
+// NaN-quieting self-max instructions on every operand.
+__device__ inline float opaque_inf() {
+  float v = __builtin_inff();
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ inline float max_nn(float x, float y, float pinf) { return __builtin_amdgcn_fmed3f(x, y, pinf); }
+
 // Reductions over the 4 lane groups sharing lane & 15 (xor 16, xor 32).
-__device__ inline float max_over_groups(float x) {
+__device__ inline float max_over_groups(float x, float pinf) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]), pinf);
 }
 __device__ inline float sum_over_groups(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

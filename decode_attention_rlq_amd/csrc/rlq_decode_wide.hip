@@ -335,6 +335,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   f4 *xch = (f4 *)(smem + kXchOff);
   auto xch_at = [&](int i, int half) -> f4 * { return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64; };
   float m_run = kNegInf, l_run = 0.f;
+  const float pinf = opaque_inf();
   f4 O[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) O[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     }
     half2v ph[4];
     auto exps = [&]() {
-      const float mb = fmaxf(m_run, -1e30f) - kBias;
+      const float mb = max_nn(m_run, -1e30f, pinf) - kBias;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         ph[2 * st] = __builtin_convertvector(
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     exps();
     // Tile max with v_med3 (med3(x, y, +inf) = max(x, y)): the scores are
     // finite or -inf here, so no NaN handling is needed.
-    auto mx = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, __builtin_inff()); };
+    auto mx = [&](float x, float y) { return max_nn(x, y, pinf); };
     float mt = mx(mx(mx(sc[0][0], sc[0][1]), mx(sc[0][2], sc[0][3])),
                   mx(mx(sc[1][0], sc[1][1]), mx(sc[1][2], sc[1][3])));
     {
