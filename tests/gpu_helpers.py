@@ -103,6 +103,27 @@ def lse_tolerance(prob, cache: oracle.Cache, ctx_lens=None) -> np.ndarray:
     return tol
 
 
+def extend_lse_tolerance(prob, cache: oracle.Cache, qc_bits, cuq, ctx_lens=None) -> np.ndarray:
+    """Per-(query row, head) LSE tolerance of an extend call, derived as in
+    lse_tolerance: max(LSE_TOL, 6 * sm_scale * 2^-11 / sqrt(3) *
+    max_{t <= p} ||q o c_hat_t||) with p the row's query position."""
+    ctx = prob.ctx_lens if ctx_lens is None else np.asarray(ctx_lens)
+    sm = float(np.float32(prob.sm_scale))
+    qc = oracle.bf16_bits_to_f64(qc_bits)
+    tol = np.full(qc.shape[:2], LSE_TOL)
+    for b, n in enumerate(ctx):
+        n, nq = int(n), int(cuq[b + 1] - cuq[b])
+        if nq == 0:
+            continue
+        c_hat, _ = oracle.gather_request(cache, prob.block_table[b], n, prob.gain, prob.level_inner,
+                                         prob.level_outer)
+        for i in range(nq):
+            pos, r = n - nq + i, int(cuq[b]) + i
+            sig = sm * 2.0 ** -11 / np.sqrt(3.0) * np.sqrt((qc[r] ** 2 @ (c_hat[:pos + 1] ** 2).T).max(axis=1))
+            tol[r] = np.maximum(LSE_TOL, 6.0 * sig)
+    return tol
+
+
 def check_decode(out, lse, ref_out, ref_lse, ctx_lens, lse_tol=LSE_TOL):
     out = out.detach().cpu().numpy().astype(np.float64)
     lse = lse.detach().cpu().numpy().astype(np.float64)

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from decode_attention_rlq_amd import rlq, workloads
-from gpu_helpers import LSE_TOL, check_decode, dev, device_cache_from, oracle_cache_for, params_of
+from gpu_helpers import check_decode, dev, device_cache_from, extend_lse_tolerance, oracle_cache_for, params_of
 
 pytestmark = pytest.mark.gpu
 
@@ -32,26 +32,6 @@ CASES = {
 
 def latents_as_z(prob):
     return (prob.latent_bits.astype(np.uint32) << 16).view(np.float32)
-
-
-def extend_lse_tolerance(prob, cache, qc_bits, cuq):
-    """Per-(query row, head) LSE tolerance from the fp16 staging of c_hat
-    (as for decode): max(LSE_TOL, 6 * sm_scale * 2^-11 / sqrt(3) *
-    max_{t <= p} ||q o c_hat_t||)."""
-    sm = float(np.float32(prob.sm_scale))
-    qc = oracle.bf16_bits_to_f64(qc_bits)
-    tol = np.full(qc.shape[:2], LSE_TOL)
-    for b, n in enumerate(prob.ctx_lens):
-        n, nq = int(n), int(cuq[b + 1] - cuq[b])
-        if nq == 0:
-            continue
-        c_hat, _ = oracle.gather_request(cache, prob.block_table[b], n, prob.gain, prob.level_inner,
-                                         prob.level_outer)
-        for i in range(nq):
-            p, r = n - nq + i, int(cuq[b]) + i
-            sig = sm * 2.0 ** -11 / np.sqrt(3.0) * np.sqrt((qc[r] ** 2 @ (c_hat[:p + 1] ** 2).T).max(axis=1))
-            tol[r] = np.maximum(LSE_TOL, 6.0 * sig)
-    return tol
 
 
 @pytest.mark.parametrize("name", list(CASES))
