@@ -227,13 +227,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     lim = row_t < qr.n_rows ? ctx - qr.n_q + row_t / A.q_heads + 1 : 0;
   }
   const Protect pt = protect_range(A, ctx);
-  const int n = it.te - it.tb;  // tiles of this item
+  // Tiles of this item that some row of the group can see: all of them for
+  // decode; for extend, up to the last query of the group (later tiles are
+  // masked for every pair, so they are not loaded at all).
+  int wg_lim = ctx;
+  if (A.cu_q != nullptr) wg_lim = ctx - qr.n_q + (min(head0 + kWideHeads, qr.n_rows) - 1) / A.q_heads + 1;
+  const int n = max(0, min(it.te, (wg_lim + kWaveTok - 1) / kWaveTok) - it.tb);
   const int pg0 = it.tb >> 1;   // first page (in the request's block table)
 
   // Page ids of the item, staged once (at most kMaxItemPages).
   int32_t *pg = (int32_t *)(smem + kPageOff);
   {
-    const int np = n > 0 ? ((it.te - 1) >> 1) - pg0 + 1 : 0;
+    const int np = n > 0 ? ((it.tb + n - 1) >> 1) - pg0 + 1 : 0;
     const int32_t *bt = A.block_table + (int64_t)b * A.max_pages + pg0;
     for (int i = threadIdx.x; i < np; i += kDecodeThreads) pg[i] = bt[i];
   }
