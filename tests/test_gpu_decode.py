@@ -46,6 +46,10 @@ DECODE_CASES = {
     "many_requests_h128": dict(name="ragged_protect", ctx_lens=[1 + 13 * b for b in range(150)], heads=128),
     # Log-uniform lengths as in the ragged workload, fewer requests.
     "ragged_h128": dict(name="ragged_protect", batch=6, heads=128),
+    # Head counts that are a multiple of 16 but not of 64 run the 16-head
+    # kernel with 3 and 7 head groups.
+    "protect_h48": dict(name="ragged_protect", ctx_lens=[70, 1030, 2500], heads=48, n_recent=16),
+    "tails_h112": dict(name="v2lite_32k", ctx_lens=[2, 65, 1500], heads=112),
 }
 
 
