@@ -2,7 +2,9 @@
 
 Each mutation swaps one oracle function for a subtly wrong variant (transposed
 operand, wrong reduction order, wrong divisor, strict comparison, wrong bit
-order, swapped levels, dropped term, missing scale).  The pins must fail.
+order, swapped levels, dropped term, missing scale, an extend that misses its
+own position, counts queries from position 0, or reads the sink / recent
+window at the query instead of the cache).  The pins must fail.
 """
 
 import numpy as np
@@ -12,6 +14,7 @@ import oracle
 import oracle.rlq_oracle as ro
 import test_oracle_attention as ta
 import test_oracle_encode as te
+import test_oracle_extend as tx
 
 
 def _patch(monkeypatch, name, fn):
@@ -66,6 +69,37 @@ def attend_without_scale(q_c, q_r, c_hat, k_r, sm_scale):
     return ORIG["attend"](q_c, q_r, c_hat, k_r, 1.0)
 
 
+def _extend_variant(limit, window_at_query=False):
+    """An extend with a planted mistake: query i attends to positions
+    [0, limit(ctx, n_q, i)); with window_at_query the sink / recent rows are
+    read as if the cache held only those positions."""
+    def extend(cache, q_c_bf16, q_r_bf16, sm_scale, block_table, ctx_lens, cu_seqlens_q, gain, level_inner,
+               level_outer):
+        qc, qr = ro.bf16_bits_to_f64(q_c_bf16), ro.bf16_bits_to_f64(q_r_bf16)
+        out = np.zeros(qc.shape)
+        lse = np.full(qc.shape[:2], -np.inf)
+        cu = np.asarray(cu_seqlens_q)
+        for b in range(len(cu) - 1):
+            n, n_q = int(ctx_lens[b]), int(cu[b + 1] - cu[b])
+            for i in range(n_q):
+                lim = limit(n, n_q, i)
+                src = lim if window_at_query else n
+                c_hat, k_r = ro.gather_request(cache, np.asarray(block_table)[b], src, gain, level_inner, level_outer)
+                c_hat = ro._protected_rows(cache, b, src, c_hat)
+                r = int(cu[b]) + i
+                out[r], lse[r] = ro.attend(qc[r], qr[r], c_hat[:lim], k_r[:lim], sm_scale)
+        return out, lse
+    return extend
+
+
+extend_excludes_own_position = _extend_variant(lambda n, n_q, i: n - n_q + i)
+extend_queries_from_position_0 = _extend_variant(lambda n, n_q, i: i + 1)
+extend_window_at_query = _extend_variant(lambda n, n_q, i: n - n_q + i + 1, window_at_query=True)
+for _f, _n in ((extend_excludes_own_position, "extend_excludes_own_position"),
+               (extend_queries_from_position_0, "extend_queries_from_position_0"),
+               (extend_window_at_query, "extend_window_at_query")):
+    _f.__name__ = _n
+
 ORIG = {n: getattr(ro, n) for n in ("group_stats", "dequant", "attend")}
 
 MUTATIONS = [
@@ -84,6 +118,15 @@ MUTATIONS = [
                                      ta.test_all_protected_equals_library_attention]),
     ("attend", attend_without_scale, [ta.test_two_tokens_follow_the_logistic,
                                       ta.test_mpmath_bruteforce_tiny_cache]),
+    ("extend", extend_excludes_own_position, [tx.test_single_query_equals_decode,
+                                              tx.test_unprotected_query_i_equals_decode_over_its_prefix,
+                                              tx.test_zero_query_is_mean_of_visible_rows_read_at_the_cache_state,
+                                              tx.test_mpmath_bruteforce_causal_tiny_cache]),
+    ("extend", extend_queries_from_position_0, [tx.test_single_query_equals_decode,
+                                                tx.test_unprotected_query_i_equals_decode_over_its_prefix,
+                                                tx.test_zero_query_is_mean_of_visible_rows_read_at_the_cache_state]),
+    # (one query per request cannot tell these windows apart: its position is the last)
+    ("extend", extend_window_at_query, [tx.test_zero_query_is_mean_of_visible_rows_read_at_the_cache_state]),
 ]
 
 
