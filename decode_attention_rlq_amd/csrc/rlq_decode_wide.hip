@@ -547,7 +547,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_wide_merge_kernel(Dec
   __shared__ float red_m[16][16], red_l[16][16];
   __shared__ f4 part[kMergeMaxTiles][kMergeWaves][64];
   const int HT = A.heads >> 4;
-  const int b = blockIdx.y / HT, ht = blockIdx.y % HT;
+  // (request, 16-row tile) index over gridDim.y x gridDim.z (the y limit is
+  // 65,535; an extend call can have more tiles).
+  const int64_t bh = blockIdx.y + (int64_t)gridDim.y * blockIdx.z;
+  if (bh >= (int64_t)A.batch * HT) return;
+  const int b = (int)(bh / HT), ht = (int)(bh % HT);
   const QueryRows qr = query_rows(A, b);
   if (16 * ht >= qr.n_rows) return;  // no such rows in this request
   const int first = A.plan[2 * b], count = A.plan[2 * b + 1];
@@ -612,8 +616,10 @@ hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t st
   // value tiles per workgroup 32 / chunks, at most kMergeMaxTiles.
   const int bht = batch * (a.heads / 16);
   int chunks = 32 / kMergeMaxTiles;
-  while (chunks < 32 && chunks * bht < 1024) chunks *= 2;
-  hipLaunchKernelGGL(decode_wide_merge_kernel, dim3(chunks, bht), dim3(64 * kMergeWaves), 0, stream, a);
+  while (chunks < 32 && (int64_t)chunks * bht < 1024) chunks *= 2;
+  const int gy = bht < 65535 ? bht : 65535;
+  hipLaunchKernelGGL(decode_wide_merge_kernel, dim3(chunks, gy, (bht + gy - 1) / gy), dim3(64 * kMergeWaves), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -228,7 +228,7 @@ static bool extend_shape(int32_t batch, int32_t heads, int32_t max_q_len, int32_
       max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX || max_q_len > max_ctx_len)
     return false;
   *rows = rlq::extend_rows(max_q_len, heads);
-  return *rows / 64 <= 65535 && (int64_t)batch * (*rows / 16) <= 65535;
+  return *rows / 64 <= 65535 && (int64_t)batch * (*rows / 16) <= (int64_t)1 << 30;
 }
 
 int rlq_mla_extend_workspace_size(int32_t batch, int32_t heads, int32_t max_q_len,

@@ -17,6 +17,9 @@
  *                        gain * level (§3.2); scores q_c.c_hat + q_R.k_R with
  *                        the read-side rotation folded into the absorbed query
  *                        (§3.3, Fig. 3a); softmax; output in latent space.
+ *   rlq_mla_extend       prefill / extend: each request's newest tokens attend
+ *                        causally to the same cache (§D: the method serves
+ *                        prefill and decode from its cache).
  *
  * Storage per unprotected token and layer: 128 B codes + 32 B fp32 group
  * statistics + 128 B BF16 RoPE key = 288 B (§A.3; the storage-accounting
@@ -238,7 +241,8 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
  * (query, head) rows, max_q_len * heads rows rounded up to 64 per request,
  * and the work-item table.  Errors: RLQ_EINVAL (heads, batch, max_q_len < 1,
  * max_ctx_len above RLQ_MAX_CTX, or a row count beyond the launch limits:
- * batch * rows / 16 and rows / 64 at most 65535).
+ * rows / 64 at most 65535 and batch * rows / 16 at most 2^30).  The partials
+ * take 32.9 KB per 16 rows and work item: chunk long prompts.
  */
 int rlq_mla_extend_workspace_size(int32_t batch, int32_t heads, int32_t max_q_len,
                                   int32_t max_ctx_len, size_t *bytes);

@@ -148,7 +148,7 @@ def test_extend_workspace_and_validation(lib):
         parts, rem = divmod(size - 8 * batch, per)
         assert rem == 0 and parts % (rows // 16) == 0 and (parts // (rows // 16)) % 8 == 0
     for bad in [(1, 24, 4, 100), (0, 16, 4, 100), (1, 16, 0, 100), (1, 16, 101, 100), (1, 144, 4, 100),
-                (64, 128, 1024, 2048)]:  # the last exceeds the launch grid
+                (1, 128, 40000, 40000)]:  # the last exceeds the launch grid (rows / 64 > 65535)
         with pytest.raises(ValueError):
             rlq.extend_workspace_size(*bad)
     p = rlq.default_params()
