@@ -179,17 +179,21 @@ def cpu_baseline_decode(prob, new_idx, sample_requests):
     oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[sel], sub_cu, np.zeros(len(reqs), np.int32), bt,
                            latent_bf16=prob.latent_bits[sel], rotation_bf16=prob.rotation_bits)
     ctx = prob.ctx_lens[reqs]
-    log("cpu baseline: timed oracle step")
+    log("cpu baseline: timed oracle steps (about 10 s)")
     t0 = time.perf_counter()
-    oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[new_idx[reqs]], np.arange(len(reqs) + 1),
-                           ctx - 1, bt, latent_bf16=prob.latent_bits[new_idx[reqs]],
-                           rotation_bf16=prob.rotation_bits)
-    oracle.decode(oc, prob.q_c_bits[reqs], prob.q_r_bits[reqs], prob.sm_scale, bt, ctx,
-                  prob.gain, prob.level_inner, prob.level_outer)
+    steps = 0
+    while steps < 8 and (steps == 0 or time.perf_counter() - t0 < 10.0):
+        # Re-appending the last position leaves the cache as it was.
+        oracle.quantize_append(oc, prob.tau, prob.k_rope_bits[new_idx[reqs]], np.arange(len(reqs) + 1),
+                               ctx - 1, bt, latent_bf16=prob.latent_bits[new_idx[reqs]],
+                               rotation_bf16=prob.rotation_bits)
+        oracle.decode(oc, prob.q_c_bits[reqs], prob.q_r_bits[reqs], prob.sm_scale, bt, ctx,
+                      prob.gain, prob.level_inner, prob.level_outer)
+        steps += 1
     dt = time.perf_counter() - t0
     toks = int(ctx.sum())
-    return {"value": toks / dt, "unit": "context tokens/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"one step (append + fp64 decode) for {len(reqs)} of {prob.batch} requests, "
+    return {"value": toks * steps / dt, "unit": "context tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{steps} step(s) (append + fp64 decode) for {len(reqs)} of {prob.batch} requests, "
                       f"{toks} context tokens, {prob.heads} heads: {dt:.2f} s"}
 
 
