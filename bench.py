@@ -15,6 +15,10 @@ Other workloads (each prints its own line with its own metric):
   --config extend_32k      prefill / extend attention of a 512-token chunk per
                            request over 4 x 32,768 cached tokens (the chunk's own
                            positions included, causal), 16 heads (MFMA-bound)
+  --config long_input      the long-input serving flow: 4 requests prefill
+                           --input-tokens prompt tokens in --prefill-chunk chunks
+                           (append + extend), then decode 128 tokens each;
+                           reports decode tokens/s after prefill and prefill tokens/s
   --config long_output     the per-step decode loop of a long generation: 4
                            requests from 128-token prompts generate --gen-tokens
                            tokens each (append the new token, decode over the grown
@@ -467,6 +471,96 @@ def bench_long_output(args, torch, rlq, workloads):
     }
 
 
+# --------------------------------------------------------------------------- long input (prefill + decode)
+
+def bench_long_input(args, torch, rlq, workloads):
+    """The long-input serving flow: 4 requests each prefill --input-tokens
+    prompt tokens in --prefill-chunk chunks (bulk quantize-append of the chunk,
+    then extend attention of its queries over the cache built so far), then
+    generate 128 tokens (append + decode per step).  Reports decode
+    throughput after prefill, and the prefill rate."""
+    dev = dev_of(torch)
+    B, H, n_in, n_out = 4, 16, args.input_tokens, 128
+    chunk = min(args.prefill_chunk, n_in)
+    log(f"generating workload long_input: {B} x {n_in}-token prompts, chunks of {chunk}, {n_out} output tokens")
+    prob = workloads.make_problem("v2lite_32k", ctx_lens=[n_in] * B, heads=H)
+    total = n_in + n_out
+    ppr = (total + 63) // 64
+    bt_np = np.random.default_rng(11).permutation(B * ppr).astype(np.int32).reshape(B, ppr)
+    p = rlq.params(prob.tau, prob.gain, prob.level_inner, prob.level_outer)
+    cache = rlq.PagedCache.allocate(B * ppr, max_batch=B)
+    bt, rot = dev(bt_np), dev(prob.rotation_bits)
+    lat, kr = dev(prob.latent_bits), dev(prob.k_rope_bits)
+    rng = np.random.default_rng(3)
+    qc = dev(workloads.to_bf16_bits(rng.standard_normal((B * chunk, H, 512), dtype=np.float32)))
+    qr = dev(workloads.to_bf16_bits(rng.standard_normal((B * chunk, H, 64), dtype=np.float32)))
+    e_out = torch.empty((B * chunk, H, 512), dtype=torch.float32, device="cuda")
+    e_lse = torch.empty((B * chunk, H), dtype=torch.float32, device="cuda")
+    e_ws = torch.zeros(rlq.extend_workspace_size(B, H, chunk, total), dtype=torch.uint8, device="cuda")
+    chunks = []
+    for c0 in range(0, n_in, chunk):
+        n = min(chunk, n_in - c0)
+        # Token rows of the chunk in the workload's latent array (request-major).
+        rows = np.concatenate([np.arange(b * n_in + c0, b * n_in + c0 + n) for b in range(B)])
+        cu = np.arange(0, B * n + 1, n, dtype=np.int32)
+        chunks.append((n, dev(prob.latent_bits[rows]), dev(prob.k_rope_bits[rows]), dev(cu),
+                       dev(np.full(B, c0, np.int32)), dev(np.full(B, c0 + n, np.int32)), c0 + n))
+    del lat, kr
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        for n, cl, ck, cu, start, ctx, c_end in chunks:
+            rlq.quantize_append(p, cache, ck, cu, start, bt, latent=cl, rotation=rot, n_tokens=B * n, stream=stream)
+            rlq.mla_extend(p, cache, qc[:B * n], qr[:B * n], cu, n, prob.sm_scale, bt, ctx, c_end,
+                           out=e_out[:B * n], lse=e_lse[:B * n], workspace=e_ws, stream=stream)
+
+    new_lat = dev(prob.latent_bits[np.arange(B) * n_in])
+    new_kr = dev(prob.k_rope_bits[np.arange(B) * n_in])
+    cu1 = dev(np.arange(B + 1, dtype=np.int32))
+    q_c, q_r = dev(prob.q_c_bits), dev(prob.q_r_bits)
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    d_ws = torch.zeros(rlq.decode_workspace_size(B, H, total), dtype=torch.uint8, device="cuda")
+    starts = [dev(np.full(B, n_in + k, np.int32)) for k in range(n_out)]
+    ctxs = [dev(np.full(B, n_in + k + 1, np.int32)) for k in range(n_out)]
+
+    def decode_step(k):
+        rlq.quantize_append(p, cache, new_kr, cu1, starts[k], bt, latent=new_lat, rotation=rot, n_tokens=B,
+                            stream=stream)
+        rlq.mla_decode(p, cache, q_c, q_r, prob.sm_scale, bt, ctxs[k], total, out=out, lse=lse, workspace=d_ws,
+                       stream=stream)
+
+    log("warmup: one prefill and the decode steps")
+    prefill()
+    for k in range(n_out):
+        decode_step(k)
+    torch.cuda.synchronize()
+    log(f"timing the prefill ({len(chunks)} chunks)")
+    ms_pre, _ = timed_loop(torch, stream, lambda i: prefill(), 1)
+    log(f"timing {n_out} decode steps")
+    ms_dec, _ = timed_loop(torch, stream, decode_step, n_out)
+    log(f"prefill {ms_pre:.1f} ms ({B * n_in / (ms_pre * 1e-3):.3g} tokens/s), decode step {ms_dec * 1e3:.1f} us")
+    ctx_end = n_in + n_out
+    alg = algorithmic_decode_bytes(B, H, [ctx_end - n_out // 2] * B)
+    gbps = alg / (ms_dec * 1e-3) / 1e9
+    return {
+        "metric": "2-bit MLA long-input serving flow: decode tokens/s after a chunked prefill "
+                  "(also prefill tokens/s)",
+        "value": B / (ms_dec * 1e-3), "unit": "generated tokens/s",
+        "n_gpus": 1, "steps": n_out, "warmup": 1, "ms_per_step": ms_dec, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"long_input: {B} requests x {n_in}-token prompts prefilled in chunks of {chunk} "
+                               f"(bulk append + extend attention), then {n_out} output tokens each (append + "
+                               f"decode), {H} heads, latent 512 + RoPE 64, 2-bit codes",
+                   "batch": B, "input_tokens": n_in, "prefill_chunk": chunk, "output_tokens": n_out, "heads": H},
+        "prefill_ms": ms_pre, "prefill_tokens_per_s": B * n_in / (ms_pre * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode step (few-token append + rlq_mla_decode) after the prefill",
+                     "algorithmic_bytes_per_launch": alg},
+    }
+
+
 # --------------------------------------------------------------------------- extend (prefill chunk)
 
 def extend_flops(heads, ctx, n_q):
@@ -578,7 +672,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="v2lite_256k",
                     choices=["v2lite_256k", "v2lite_32k", "ragged_protect", "append_bulk", "long_output",
-                             "extend_32k"])
+                             "extend_32k", "long_input"])
+    ap.add_argument("--input-tokens", type=int, default=32768, help="long_input: prompt tokens per request")
+    ap.add_argument("--prefill-chunk", type=int, default=4096, help="long_input: prefill chunk (tokens)")
     ap.add_argument("--chunk", type=int, default=512, help="extend_32k: new (query) tokens per request")
     ap.add_argument("--gen-tokens", type=int, default=262144,
                     help="long_output: tokens generated per request")
@@ -619,6 +715,8 @@ def main():
         res = bench_long_output(args, torch, rlq, workloads)
     elif args.config == "extend_32k":
         res = bench_extend(args, torch, rlq, workloads)
+    elif args.config == "long_input":
+        res = bench_long_input(args, torch, rlq, workloads)
     else:
         res = bench_decode(args, torch, rlq, workloads)
     print(json.dumps(res), flush=True)
