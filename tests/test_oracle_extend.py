@@ -140,3 +140,33 @@ def test_requests_without_queries_are_skipped():
     out, lse = oracle.extend(cache, qc, qr, 0.2, bt, lens, [0, 0, 4, 4], 1.0, A_IN, A_OUT)
     o, l = oracle.extend(cache, qc, qr, 0.2, bt[1:2], lens[1:2], [0, 4], 1.0, A_IN, A_OUT)
     assert np.array_equal(out, o) and np.array_equal(lse, l)
+
+
+def test_repeated_page_is_one_copy_merged_in_closed_form():
+    """A block table that names one page for every position makes the context
+    that page repeated.  Softmax over R copies plus a t-token prefix has a
+    closed form (the LSE gains log R for the copies, then a two-term log-sum-
+    exp merge with the prefix); the oracle must reach it exactly, for every
+    query position including the ones on a page boundary."""
+    rng = np.random.default_rng(31)
+    page = 4
+    cache, _, _, bt = build(rng, [page], page=page)
+    n_q, reps = 6, 5
+    ctx = reps * page + 2
+    big_bt = np.zeros((1, (ctx + page - 1) // page), np.int32) + bt[0, 0]
+    qc, qr = rand_bf16(rng, (n_q, 2, 32)), rand_bf16(rng, (n_q, 2, 4))
+    cu = np.array([0, n_q], np.int32)
+    out, lse = oracle.extend(cache, qc, qr, 0.3, big_bt, [ctx], cu, 1.1, A_IN, A_OUT)
+    for i in range(n_q):
+        n = ctx - n_q + i + 1
+        r, t = divmod(n, page)
+        one = np.array([0, 1], np.int32)
+        o_p, l_p = oracle.extend(cache, qc[i:i + 1], qr[i:i + 1], 0.3, bt, [page], one, 1.1, A_IN, A_OUT)
+        want_l, want_o = l_p[0] + math.log(r), o_p[0]
+        if t:
+            o_t, l_t = oracle.extend(cache, qc[i:i + 1], qr[i:i + 1], 0.3, bt, [t], one, 1.1, A_IN, A_OUT)
+            merged = np.logaddexp(want_l, l_t[0])
+            want_o = np.exp(want_l - merged)[:, None] * want_o + np.exp(l_t[0] - merged)[:, None] * o_t[0]
+            want_l = merged
+        np.testing.assert_allclose(lse[i], want_l, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out[i], want_o, rtol=0, atol=1e-12)
