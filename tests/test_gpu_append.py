@@ -61,6 +61,13 @@ CASES = {
     # requests, start offsets and protection.
     "bulk_ragged": dict(name="tiny", ctx_lens=[1500, 3070, 7, 900, 2100], start=[0, 60, 0, 33, 64],
                         n_sink=4, n_recent=16),
+    # The bulk kernel with more requests than its LDS request table holds
+    # (2047): the request search runs on global memory; every ninth request
+    # has no new token.
+    "bulk_many_requests": dict(name="tiny", ctx_lens=[1 + (5 * b + b // 7) % 6 for b in range(2100)],
+                               start=[(1 + (5 * b + b // 7) % 6) if b % 9 == 0 else
+                                      (b % 2) * min(1, (5 * b + b // 7) % 6) for b in range(2100)],
+                               n_sink=1, n_recent=3),
 }
 
 
