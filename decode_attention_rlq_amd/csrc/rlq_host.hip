@@ -135,10 +135,16 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
   return hip_status(rlq::launch_append(a, (hipStream_t)stream));
 }
 
+// The 16-head kernel launches one workgroup row per (request, head group) in
+// a grid dimension of at most 65535; the many-head kernel has no such bound.
+static bool decode_shape(int32_t batch, int32_t heads) {
+  if (batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16) return false;
+  return rlq::use_wide(heads) || (int64_t)batch * (heads / 16) <= 65535;
+}
+
 int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
                                   size_t *bytes) {
-  if (bytes == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16 ||
-      max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX)
+  if (bytes == nullptr || !decode_shape(batch, heads) || max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX)
     return RLQ_EINVAL;
   *bytes = rlq::use_wide(heads)
                ? rlq::wide_workspace_bytes(batch, heads, rlq::plan_wide(batch, heads, max_ctx_len))
@@ -153,8 +159,7 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
                    const int32_t *ctx_lens, int32_t max_ctx_len,
                    float *out, float *lse,
                    void *workspace, size_t workspace_bytes, void *stream) {
-  if (p == nullptr || batch < 1 || heads < 16 || heads > RLQ_MAX_HEADS || heads % 16)
-    return RLQ_EINVAL;
+  if (p == nullptr || !decode_shape(batch, heads)) return RLQ_EINVAL;
   if (max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX || max_pages_per_req < 1 ||
       (int64_t)max_ctx_len > (int64_t)max_pages_per_req * RLQ_PAGE)
     return RLQ_EINVAL;

@@ -192,7 +192,8 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
  * maximum context length: split-KV partials (unnormalised output, running max
  * and sum per split and head) and, when heads is a multiple of 64, a table of
  * each request's work items (two int32 per request).  Errors: RLQ_EINVAL (also
- * for max_ctx_len above RLQ_MAX_CTX).
+ * for max_ctx_len above RLQ_MAX_CTX, and for batch * heads / 16 above 65535
+ * when heads is not a multiple of 64).
  */
 int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_len,
                                   size_t *bytes);
@@ -214,7 +215,9 @@ int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_
  *   q_r_bf16       device [batch][heads][64] RoPE queries (BF16)
  *   heads          multiple of 16, at most 128 (a multiple of 64 runs the
  *                  many-head kernel: each token decoded once per 64 heads,
- *                  work items balanced over ctx_lens on the device)
+ *                  work items balanced over ctx_lens on the device; other
+ *                  counts run the 16-head kernel, which takes at most 65535
+ *                  (request, 16-head group) pairs per call)
  *   sm_scale       softmax scale
  *   block_table    device int32 [batch][max_pages_per_req]
  *   ctx_lens       device int32 [batch], 0 <= ctx_lens[b] <= max_ctx_len

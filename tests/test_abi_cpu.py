@@ -72,6 +72,14 @@ def test_workspace_size(lib):
         rlq.decode_workspace_size(0, 16, 100)
     with pytest.raises(ValueError):
         rlq.decode_workspace_size(1, 144, 100)
+    # The 16-head kernel's grid holds at most 65535 (request, head group)
+    # pairs; the many-head kernel (heads a multiple of 64) has no such bound.
+    assert rlq.decode_workspace_size(65535, 16, 100) > 0
+    assert rlq.decode_workspace_size(21845, 48, 100) > 0
+    assert rlq.decode_workspace_size(100000, 64, 100) > 0
+    for bad in ((65536, 16, 100), (21846, 48, 100)):
+        with pytest.raises(ValueError):
+            rlq.decode_workspace_size(*bad)
 
 
 @pytest.mark.parametrize("batch,heads,ctx", [(32, 112, 59297), (1, 16, 1 << 20), (4, 16, 262144),
