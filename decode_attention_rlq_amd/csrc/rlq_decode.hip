@@ -214,6 +214,14 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   half8 qB[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) qB[k] = *(const half8 *)(smem + qslot(r16, 8 * h + k, g4));
+  // The query in fp8 for the score correction of decoded tokens (BF16 sink /
+  // recent rows convert to fp16 exactly and need none).
+  constexpr bool kCorr = !kProt;
+  u2 q8B[8];
+  if constexpr (kCorr) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q8B[k] = query_fp8(qB[k]);
+  }
   // Exchange slots of partial scores, [pair][parity][half][sub-tile][64 lanes].
   // A slot holding kPoison in any element is empty: the reader re-poisons a
   // slot after consuming it, so readiness needs no flag and no barrier.
@@ -344,14 +352,18 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     constexpr bool kScore = decltype(score_c)::value;
     constexpr bool kValue = decltype(value_c)::value;
     f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    // The correction accumulates apart (fp8 MFMAs only) and joins with a
+    // VALU add at the end of the tile.
+    f4 accR[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
     auto score_pair = [&](int p) {
 #pragma unroll
       for (int kl = 2 * p; kl < 2 * p + 2; ++kl)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const u4 v = dec(kl, st);
-          *(u4 *)(wl + st * kSubBytes + kl * 1024 + 16 * chat_slot(kl, g4, r16)) = v;
-          acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), qB[kl], acc[st], 0, 0, 0);
+          const Dec8 v = dec(kl, st);
+          *(u4 *)(wl + st * kSubBytes + kl * 1024 + 16 * chat_slot(kl, g4, r16)) = v.v;
+          acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v.v), qB[kl], acc[st], 0, 0, 0);
+          if constexpr (kCorr) accR[st] = correct_scores(v.r, q8B[kl], accR[st]);
         }
     };
     half8 av0[4];
@@ -395,15 +407,16 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
       if constexpr (kValue) value_pair(p, av);
     }
     if constexpr (kScore) {
+      mfma_type_switch();  // f16 -> bf16 on acc
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
       tail();
-      acc_prev[0] = acc[0];
-      acc_prev[1] = acc[1];
+      acc_prev[0] = kCorr ? acc[0] + accR[0] : acc[0];
+      acc_prev[1] = kCorr ? acc[1] + accR[1] : acc[1];
     }
   };
-  auto no_dec = [](int, int) -> u4 { return u4{0, 0, 0, 0}; };
+  auto no_dec = [](int, int) -> Dec8 { return Dec8{u4{0, 0, 0, 0}, u2{0, 0}}; };
   auto no_tail = []() {};
   const u4 no_rp[2] = {};
 
@@ -427,7 +440,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     auto run = [&](auto value_c, const CodeLoad &cur, const CodeLoad &next, CodeLoad &far, int i) {
       load_rope(A, tile_slot(i), r16, g4, h, rb);
       load_codes(A, tile_slot(i + 2), r16, g4, h, far);
-      auto dec = [&](int kl, int st) -> u4 {
+      auto dec = [&](int kl, int st) -> Dec8 {
         return decode8(cur.cw[st][(kl >> 1) & 3], kl & 1, lut[st]);
       };
       auto tail = [&]() { build_lut(next, i + 1); };
@@ -468,12 +481,12 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
           rp[st] = *(const u4 *)(A.rope + slot * RLQ_DR + 16 * g4 + 8 * h);
         }
       }
-      auto dec = [&](int kl, int st) -> u4 {
-        if (row[st] == nullptr) return u4{0, 0, 0, 0};
+      auto dec = [&](int kl, int st) -> Dec8 {
+        if (row[st] == nullptr) return Dec8{u4{0, 0, 0, 0}, u2{0, 0}};
         const int word = 4 * (q0 + 2 * h) + ((kl >> 1) & 3);
         const u4 w0 = *(const u4 *)(row[st] + 16 * word);
         const u4 w1 = *(const u4 *)(row[st] + 16 * word + 8);
-        return convert8(w0, w1, kl & 1);
+        return Dec8{convert8(w0, w1, kl & 1), u2{0, 0}};
       };
       if (i == 0)
         step(bool_c<true>{}, bool_c<false>{}, dec, rp, i, 0, 0, t_end, no_tail);
@@ -533,19 +546,17 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   }
 }
 
-// Splits of a cache without sink/recent buffers.
+// The ordinary splits of every (request, head group): partials prot .. prot +
+// splits - 1.
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_kernel(DecodeArgs A) {
   split_body<false>(A, (int)blockIdx.x);
 }
 
-// With sink/recent buffers, one launch holds both kinds of workgroup:
-// blockIdx.x = 0 covers the BF16 sink/recent tokens (partial 0), the others
-// the ordinary splits.
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_split_prot_kernel(DecodeArgs A) {
-  if (blockIdx.x == 0)
-    split_body<true>(A, -1);
-  else
-    split_body<false>(A, (int)blockIdx.x - 1);
+// The BF16 sink/recent tokens of each (request, head group): partial 0,
+// launched before the ordinary splits (kept apart from them so each kernel is
+// allocated only the registers of its own path).
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode_prot_kernel(DecodeArgs A) {
+  split_body<true>(A, -1);
 }
 
 // The standalone merge: 32 workgroups of 4 waves per (request, head group).
@@ -601,19 +612,19 @@ size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &pla
 hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    for (const void *f : {(const void *)decode_split_kernel, (const void *)decode_split_prot_kernel}) {
+    for (const void *f : {(const void *)decode_split_kernel, (const void *)decode_prot_kernel}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return e;
     }
     attr_set = true;
   }
   const int hg = a.heads / 16;
-  if (a.prot)
-    hipLaunchKernelGGL(decode_split_prot_kernel, dim3(a.splits + 1, batch, hg), dim3(kDecodeThreads), kLdsBytes,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel, dim3(a.splits, batch, hg), dim3(kDecodeThreads), kLdsBytes, stream,
-                       a);
+  if (a.prot) {
+    hipLaunchKernelGGL(decode_prot_kernel, dim3(1, batch, hg), dim3(kDecodeThreads), kLdsBytes, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decode_split_kernel, dim3(a.splits, batch, hg), dim3(kDecodeThreads), kLdsBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(32, batch * hg), dim3(64 * kMergeWaves), 0, stream, a);

@@ -93,34 +93,94 @@ __device__ inline float sum_over_groups(float x) {
 }
 
 // Table of one (token, group): low bytes and high bytes of the four fp16
-// values, so v_perm_b32 can look both up with 2-bit selectors.
+// values, so v_perm_b32 can look both up with 2-bit selectors, and the four
+// residuals t - fp16(t) of the fp32 table entries t, each rounded to bf8
+// (OCP e5m2) in one byte.  The fp16 value carries a relative rounding error
+// of up to 2^-12, which a score contracting 512 such values over a near tie
+// of two tokens can no longer afford; the residual takes it down to ~2^-15
+// (bf8 keeps 3 significant bits of it) in a second, 8-bit contraction.  The
+// value product uses the fp16 value alone.
 struct Lut {
-  uint32_t lo, hi;
+  uint32_t lo, hi, rs;
 };
 __device__ inline Lut make_lut(float mu, float s, float gain, float a, float b, bool valid) {
   const float sg = s * gain;
-  const uint32_t p01 = h16(mu - sg * b) | (h16(mu - sg * a) << 16);
-  const uint32_t p23 = h16(mu + sg * a) | (h16(mu + sg * b) << 16);
+  const float t0 = __builtin_fmaf(-sg, b, mu), t1 = __builtin_fmaf(-sg, a, mu);
+  const float t2 = __builtin_fmaf(sg, a, mu), t3 = __builtin_fmaf(sg, b, mu);
+  const _Float16 h0 = (_Float16)t0, h1 = (_Float16)t1, h2 = (_Float16)t2, h3 = (_Float16)t3;
+  const uint32_t p01 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  const uint32_t p23 = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+  // t - fp16(t) is exact in fp32 (fp16(t) is t cut to 11 significant bits).
+  uint32_t rs = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(t0 - (float)h0, t1 - (float)h1, 0, false);
+  rs = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(t2 - (float)h2, t3 - (float)h3, (int)rs, true);
   Lut l;
   l.lo = valid ? __builtin_amdgcn_perm(p23, p01, 0x06040200u) : 0u;
   l.hi = valid ? __builtin_amdgcn_perm(p23, p01, 0x07050301u) : 0u;
+  l.rs = valid ? rs : 0u;
   return l;
 }
 
 // Codes 2h, 2h+4, 2h+8, 2h+12, 2h+1, 2h+5, 2h+9, 2h+13 of word w as eight
-// fp16 values (operand slots 0..7).
-__device__ inline u4 decode8(uint32_t w, int h, const Lut &l) {
+// fp16 values (operand slots 0..7) and, in the same slots, their eight bf8
+// residuals (the operand of the score correction).
+struct Dec8 {
+  u4 v;
+  u2 r;
+};
+__device__ inline Dec8 decode8(uint32_t w, int h, const Lut &l) {
   const uint32_t y0 = (w >> (4 * h)) & 0x03030303u;
   const uint32_t y1 = (w >> (4 * h + 2)) & 0x03030303u;
   const uint32_t lo0 = __builtin_amdgcn_perm(0u, l.lo, y0);
   const uint32_t hi0 = __builtin_amdgcn_perm(0u, l.hi, y0);
   const uint32_t lo1 = __builtin_amdgcn_perm(0u, l.lo, y1);
   const uint32_t hi1 = __builtin_amdgcn_perm(0u, l.hi, y1);
-  u4 r;
-  r[0] = __builtin_amdgcn_perm(hi0, lo0, 0x05010400u);
-  r[1] = __builtin_amdgcn_perm(hi0, lo0, 0x07030602u);
-  r[2] = __builtin_amdgcn_perm(hi1, lo1, 0x05010400u);
-  r[3] = __builtin_amdgcn_perm(hi1, lo1, 0x07030602u);
+  Dec8 d;
+  d.v[0] = __builtin_amdgcn_perm(hi0, lo0, 0x05010400u);
+  d.v[1] = __builtin_amdgcn_perm(hi0, lo0, 0x07030602u);
+  d.v[2] = __builtin_amdgcn_perm(hi1, lo1, 0x05010400u);
+  d.v[3] = __builtin_amdgcn_perm(hi1, lo1, 0x07030602u);
+  d.r[0] = __builtin_amdgcn_perm(0u, l.rs, y0);
+  d.r[1] = __builtin_amdgcn_perm(0u, l.rs, y1);
+  return d;
+}
+
+// The eight bf8 residuals of decode8(w, h, l) alone (for a wave that scores
+// c_hat decoded by another wave).
+__device__ inline u2 resid8(uint32_t w, int h, uint32_t rs) {
+  u2 r;
+  r[0] = __builtin_amdgcn_perm(0u, rs, (w >> (4 * h)) & 0x03030303u);
+  r[1] = __builtin_amdgcn_perm(0u, rs, (w >> (4 * h + 2)) & 0x03030303u);
+  return r;
+}
+
+// Gap between two MFMAs of different types chained on one accumulator.  On
+// gfx950 an MFMA that takes its accumulator (srcC) straight from the result
+// of an MFMA of another type (f16, bf16, bf8 x fp8) reads a wrong value unless
+// about six wait states separate the two (measured: four fail, six suffice);
+// the compiler assumes an exactly overlapping srcC is forwarded and inserts
+// none.  The nop is fenced so no instruction moves across it.
+__device__ inline void mfma_type_switch() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Score correction of one K-step: acc += r^T q8, with r the bf8 residuals of
+// the c_hat operand (same slots) and q8 the query rounded to fp8 (OCP e4m3).
+__device__ inline f4 correct_scores(const u2 &r, const u2 &q8, const f4 &acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(__builtin_bit_cast(long, r), __builtin_bit_cast(long, q8), acc,
+                                                      0, 0, 0);
+}
+
+// Eight fp16 query values of an operand slot as fp8 (OCP e4m3, nearest).
+__device__ inline u2 query_fp8(const half8 &q) {
+  u2 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32((float)q[4 * i], (float)q[4 * i + 1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32((float)q[4 * i + 2], (float)q[4 * i + 3], v, true);
+    r[i] = (uint32_t)v;
+  }
   return r;
 }
 

@@ -40,7 +40,15 @@ constexpr int kBufs = 3;
 constexpr int kXchOff = kBufs * (kCBufBytes + kRopeBufBytes);
 constexpr int kWideXchBytes = kWidePairs * 2 * 2 * 2 * 64 * 16;  // [pair][parity][half][sub-tile][lane]
 constexpr int kPageOff = kXchOff + kWideXchBytes;
-constexpr int kWideLds = kPageOff + kMaxItemPages * 4;  // 144 KB: one workgroup per CU
+// Code words and bf8 residual tables of a tile, for the score correction:
+// token row t holds its 32 code words at t * kCodeRow (rows padded so the 16
+// rows of one 16-byte read start in distinct bank groups), then the tables
+// [32 tokens][4 groups] (uint32: four bf8 residuals each).
+constexpr int kCodeRow = RLQ_WORDS * 4 + 16;
+constexpr int kCodeTabOff = kWaveTok * kCodeRow;
+constexpr int kCodeBufBytes = kCodeTabOff + kWaveTok * 4 * 4;  // 5 KB
+constexpr int kCodeOff = kPageOff + kMaxItemPages * 4;
+constexpr int kWideLds = kCodeOff + kBufs * kCodeBufBytes;  // 159 KB: one workgroup per CU
 static_assert(kWideLds <= 160 * 1024, "LDS budget");
 constexpr int kQHead = 16 * 4 * 16 + 16;  // query staging: bytes per head row (padded)
 static_assert(kWideHeads * kQHead <= kXchOff, "query staging fits the c_hat buffers");
@@ -263,6 +271,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
 #pragma unroll
   for (int k = 0; k < 8; ++k) qB[k] = *(const half8 *)(smem + qslot(16 * pr + r16, 8 * h + k, g4));
   __syncthreads();  // query staging done: the buffers below may be overwritten
+  // The query in fp8 for the score correction.
+  u2 q8B[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q8B[k] = query_fp8(qB[k]);
 
   // ---- fill role of this lane: sub-tile fst, 128-coordinate group fgrp,
   // token row fr, code words W0, W0 + 1 (coordinates 16 W0 .. 16 W0 + 31).
@@ -295,6 +307,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   // c_hat and RoPE buffers of ring slot k (tile i lives in slot i % 3).
   auto cbuf = [&](int k) -> unsigned char * { return smem + k * kCBufBytes; };
   auto rbuf = [&](int k) -> unsigned char * { return smem + kBufs * kCBufBytes + k * kRopeBufBytes; };
+  auto codebuf = [&](int k) -> unsigned char * { return smem + kCodeOff + k * kCodeBufBytes; };
   // Fill of tile i (into ring slot k) in parts, so the iteration can
   // interleave its decoding with the MFMAs: the table (fill_lut), the four
   // 16-byte slots (fill_part), then the RoPE copy and, in tiles that hold sink
@@ -305,11 +318,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     return make_lut(F.mu, F.sd, A.gain, A.level_inner, A.level_outer, pos < ctx);
   };
   auto fill_part = [&](int k, const FillLoad &F, const Lut &l, int e2) {
-    *(u4 *)(cbuf(k) + fill_slot(W0 + (e2 >> 1), e2 & 1, fst, fr)) = decode8(F.cw[e2 >> 1], e2 & 1, l);
+    *(u4 *)(cbuf(k) + fill_slot(W0 + (e2 >> 1), e2 & 1, fst, fr)) = decode8(F.cw[e2 >> 1], e2 & 1, l).v;
   };
-  auto fill_end = [&](int i, int k, const FillLoad &F) {
+  auto fill_end = [&](int i, int k, const FillLoad &F, const Lut &l) {
     // RoPE key: 8 bytes of token rtok, chunk ru >> 1.
     *(u2 *)(rbuf(k) + rope_off(rtok, ru >> 1) + 8 * (ru & 1)) = F.rp;
+    // Code words and residual table of (token ftok, group fgrp) for the
+    // scoring waves' correction; BF16 rows below need none (table 0).
+    *(u2 *)(codebuf(k) + ftok * kCodeRow + 4 * W0) = F.cw;
+    uint32_t rs = l.rs;
     if constexpr (kProt) {
       const int pos0 = kWaveTok * (it.tb + i);
       if (pos0 < pt.ns || pos0 + kWaveTok > ctx - pt.nr) {
@@ -324,16 +341,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
             const u4 w1 = *(const u4 *)(row + 16 * (W0 + w) + 8);
             *(u4 *)(cbuf(k) + fill_slot(W0 + w, 0, fst, fr)) = convert8(w0, w1, 0);
             *(u4 *)(cbuf(k) + fill_slot(W0 + w, 1, fst, fr)) = convert8(w0, w1, 1);
+            __builtin_amdgcn_sched_barrier(0);  // one word's rows in registers at a time
           }
+          rs = 0u;
         }
       }
     }
+    if (g4 == 0) *(uint32_t *)(codebuf(k) + kCodeTabOff + 4 * (4 * ftok + fgrp)) = rs;
   };
   auto fill = [&](int i, int k, const FillLoad &F) {
     const Lut l = fill_lut(i, F);
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) fill_part(k, F, l, e2);
-    fill_end(i, k, F);
+    fill_end(i, k, F, l);
   };
 
   // ---- pair state
@@ -345,19 +365,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
 #pragma unroll
   for (int i = 0; i < 16; ++i) O[i] = f4{0.f, 0.f, 0.f, 0.f};
   half8 PB = {};
-  f4 acc_prev[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
   // Transposed-read offset of this lane (see the 16-head kernel): lane p = r16
   // of lane group g4 supplies token row 4*g4 + p/4 of each sub-tile and
   // coordinates q = p % 4.
   const int va = (r16 & 3) >> 1;
   const int vrd = 1024 * va + 16 * ((4 * g4 + (r16 >> 2)) ^ (8 * va)) + 8 * (r16 & 1);
+  const int wq0 = 4 * (g4 >> 1) + (g4 & 1);  // this lane's 16-byte run of code words (coord_of)
 
-  // Lazy online softmax of the pair's tile (own partial scores in acc_prev,
+  // Lazy online softmax of the pair's tile (own partial scores in m0, m1,
   // the partner's in o0, o1); both waves compute the same values.
-  auto softmax = [&](const f4 &o0, const f4 &o1, int c0) {
+  auto softmax = [&](const f4 &m0, const f4 &m1, const f4 &o0, const f4 &o1, int c0) {
     f4 sc[2];
-    sc[0] = h == 0 ? acc_prev[0] + o0 : o0 + acc_prev[0];
-    sc[1] = h == 0 ? acc_prev[1] + o1 : o1 + acc_prev[1];
+    sc[0] = h == 0 ? m0 + o0 : o0 + m0;
+    sc[1] = h == 0 ? m1 + o1 : o1 + m1;
     // sc[st][j] = raw score of position c0 + 16*st + 4*g4 + j, head r16.
     // Positions past the context (or, for extend, past the query) score -inf.
     if (c0 + kWaveTok > lim) {
@@ -451,15 +471,32 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
           acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v), qB[kl], acc[st], 0, 0, 0);
         }
     };
+    // Score correction of tile i, after all its f16 products: lane (r16, g4)
+    // scores token 16 st + r16 with code words 4 q0 + 8h .. + 3 (K-step kl
+    // uses word kl / 2) of group 2 (g4 >> 1) + h and that group's residual
+    // table, both read back from the tile's code buffer.
+    const unsigned char *cb = codebuf(k);
+    auto correct = [&]() {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u4 wv = *(const u4 *)(cb + (16 * st + r16) * kCodeRow + 4 * (4 * wq0 + 8 * h));
+        const uint32_t rt = *(const uint32_t *)(cb + kCodeTabOff + 4 * (4 * (16 * st + r16) + 2 * (g4 >> 1) + h));
+#pragma unroll
+        for (int kl = 0; kl < 8; ++kl) acc[st] = correct_scores(resid8(wv[kl >> 1], kl & 1, rt), q8B[kl], acc[st]);
+      }
+    };
     Lut fl;
     if constexpr (kScore) fl = fill_lut(i + 1, F);
     half8 av0[4];
     if constexpr (kValue) {
-      const f4 *other = xch_at(i - 1, h ^ 1);
+      // Both partials of tile i-1 come back from the exchange slots (the own
+      // one too: the slots of tile i-1 are rewritten only in iteration i+1).
+      const f4 *other = xch_at(i - 1, h ^ 1), *own = xch_at(i - 1, h);
       const f4 o0 = other[lane], o1 = other[64 + lane];
-      tr_pair(vw, 0, av0);
+      const f4 m0 = own[lane], m1 = own[64 + lane];
       if constexpr (kScore) score_pair(0);
-      softmax(o0, o1, kWaveTok * (it.tb + i - 1));
+      softmax(m0, m1, o0, o1, kWaveTok * (it.tb + i - 1));
+      tr_pair(vw, 0, av0);
       value_pair(0, av0);
     } else if constexpr (kScore) {
       score_pair(0);
@@ -474,18 +511,20 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
     }
     if constexpr (kScore) {
       const unsigned char *rb = rbuf(k);
+      u4 rp[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const u4 rp = *(const u4 *)(rb + rope_off(16 * st + r16, 2 * g4 + h));
-        acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp), qrB, acc[st], 0, 0, 0);
-      }
+      for (int st = 0; st < 2; ++st) rp[st] = *(const u4 *)(rb + rope_off(16 * st + r16, 2 * g4 + h));
+      mfma_type_switch();  // f16 -> bf8 x fp8 on acc
+      correct();
+      mfma_type_switch();  // bf8 x fp8 -> bf16 on acc
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
       fill_part(kn, F, fl, 3);
-      fill_end(i + 1, kn, F);
+      fill_end(i + 1, kn, F, fl);
       f4 *mine = xch_at(i, h);
       mine[lane] = acc[0];
       mine[64 + lane] = acc[1];
-      acc_prev[0] = acc[0];
-      acc_prev[1] = acc[1];
       __builtin_amdgcn_sched_barrier(0);
       load_fill(i + 4, F);
       __builtin_amdgcn_sched_barrier(0);

@@ -77,54 +77,9 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
-def lse_tolerance(prob, cache: oracle.Cache, ctx_lens=None) -> np.ndarray:
-    """Per-(request, head) LSE tolerance derived from the kernels' arithmetic.
-
-    The kernels stage c_hat in fp16: each coordinate carries a rounding error
-    of at most 2^-11 relative, which spreads like a uniform variable (standard
-    deviation 2^-11 / sqrt 3 relative), so score t of head h is off by about
-    sigma_t = sm_scale * 2^-11 / sqrt(3) * ||q_h o c_hat_t||_2.  The LSE is a
-    softmax-weighted mean of the score errors (to first order), so its error
-    has a standard deviation of at most max_t sigma_t; with one token in the
-    context it is exactly that score's error.  Tolerance: max(LSE_TOL,
-    6 max_t sigma_t)."""
-    ctx = prob.ctx_lens if ctx_lens is None else np.asarray(ctx_lens)
-    sm = float(np.float32(prob.sm_scale))
-    qc = oracle.bf16_bits_to_f64(prob.q_c_bits)
-    tol = np.full(qc.shape[:2], LSE_TOL)
-    for b, n in enumerate(ctx):
-        n = int(n)
-        if n == 0:
-            continue
-        c_hat, _ = oracle.gather_request(cache, prob.block_table[b], n, prob.gain, prob.level_inner,
-                                         prob.level_outer)
-        sig = sm * 2.0 ** -11 / np.sqrt(3.0) * np.sqrt((qc[b] ** 2 @ (c_hat ** 2).T).max(axis=1))
-        tol[b] = np.maximum(LSE_TOL, 6.0 * sig)
-    return tol
-
-
-def extend_lse_tolerance(prob, cache: oracle.Cache, qc_bits, cuq, ctx_lens=None) -> np.ndarray:
-    """Per-(query row, head) LSE tolerance of an extend call, derived as in
-    lse_tolerance: max(LSE_TOL, 6 * sm_scale * 2^-11 / sqrt(3) *
-    max_{t <= p} ||q o c_hat_t||) with p the row's query position."""
-    ctx = prob.ctx_lens if ctx_lens is None else np.asarray(ctx_lens)
-    sm = float(np.float32(prob.sm_scale))
-    qc = oracle.bf16_bits_to_f64(qc_bits)
-    tol = np.full(qc.shape[:2], LSE_TOL)
-    for b, n in enumerate(ctx):
-        n, nq = int(n), int(cuq[b + 1] - cuq[b])
-        if nq == 0:
-            continue
-        c_hat, _ = oracle.gather_request(cache, prob.block_table[b], n, prob.gain, prob.level_inner,
-                                         prob.level_outer)
-        for i in range(nq):
-            pos, r = n - nq + i, int(cuq[b]) + i
-            sig = sm * 2.0 ** -11 / np.sqrt(3.0) * np.sqrt((qc[r] ** 2 @ (c_hat[:pos + 1] ** 2).T).max(axis=1))
-            tol[r] = np.maximum(LSE_TOL, 6.0 * sig)
-    return tol
-
-
-def check_decode(out, lse, ref_out, ref_lse, ctx_lens, lse_tol=LSE_TOL):
+def check_decode(out, lse, ref_out, ref_lse, ctx_lens):
+    """Output within OUT_TOL (row-normalised) and LSE within LSE_TOL of the
+    oracle; empty contexts give 0 and -inf."""
     out = out.detach().cpu().numpy().astype(np.float64)
     lse = lse.detach().cpu().numpy().astype(np.float64)
     ctx = np.asarray(ctx_lens)
@@ -137,10 +92,7 @@ def check_decode(out, lse, ref_out, ref_lse, ctx_lens, lse_tol=LSE_TOL):
     lerr = float(np.abs(lse[full] - ref_lse[full]).max()) if full.any() else 0.0
     assert np.isfinite(out).all()
     assert err <= OUT_TOL, f"output row-relative error {err:.3e} > {OUT_TOL}"
-    tol = np.broadcast_to(np.asarray(lse_tol, dtype=np.float64), lse.shape)
-    excess = np.abs(lse[full] - ref_lse[full]) - tol[full]
-    assert excess.size == 0 or excess.max() <= 0, \
-        f"lse error {lerr:.3e} above its tolerance (by {excess.max():.3e})"
+    assert lerr <= LSE_TOL, f"lse error {lerr:.3e} > {LSE_TOL}"
     return err, lerr
 
 

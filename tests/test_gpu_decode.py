@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from decode_attention_rlq_amd import rlq, workloads
-from gpu_helpers import (check_decode, lse_tolerance, dev, device_cache_from, empty_device_cache, oracle_cache_for,
+from gpu_helpers import (check_decode, dev, device_cache_from, empty_device_cache, oracle_cache_for,
                          oracle_decode, params_of, run_decode)
 
 pytestmark = pytest.mark.gpu
@@ -53,31 +53,57 @@ DECODE_CASES = {
     # More requests (300) than the 16-head kernel's workgroups of one round:
     # one split per request; then a 20,000-token request among them needs two
     # (a split holds at most 16384 tokens).
+    # Request 77, head 8 of this input has a near tie (two tokens hold 0.39
+    # and 0.33 of the softmax): with fp16 c_hat alone in the scores it reached
+    # 2.2e-3 (tests/test_precision_model.py reproduces it on the host).
     "many_requests_h16": dict(name="v2lite_32k", ctx_lens=[1 + 7 * b for b in range(300)]),
     "long_among_many_h16": dict(name="ragged_protect", ctx_lens=[20000] + [64 + b for b in range(300)], heads=16),
 }
 
 
-# Known precision gap: on this input one row in 4800 (request 77, head 8: two
-# tokens hold 0.39 and 0.33 of the softmax) reaches a row-normalised error of
-# 2.2e-3.  A host emulation of the kernels' fp16 rounding of c_hat reproduces it
-# (2.3e-3, of which 2.0e-3 comes from the scores alone), so it is the score
-# operand's precision, not a kernel fault.
-FP16_SCORE_GAP = {"many_requests_h16"}
-
-
-@pytest.mark.parametrize("case", [
-    pytest.param(c, marks=pytest.mark.xfail(reason="fp16 c_hat score operand: 2.2e-3 on one near-tie row",
-                                            strict=False)) if c in FP16_SCORE_GAP else c
-    for c in DECODE_CASES])
+@pytest.mark.parametrize("case", list(DECODE_CASES))
 def test_decode_oracle_cache(case):
     kw = dict(DECODE_CASES[case])
     prob = workloads.make_problem(kw.pop("name"), **kw)
     oc, _ = oracle_cache_for(prob, z=z_of(prob))
     ref_out, ref_lse = oracle_decode(prob, oc)
     out, lse = run_decode(prob, device_cache_from(oc))
-    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
     print(f"{case}: out err {err:.2e}, lse err {lerr:.2e}")
+
+
+def peaked(prob, scale=3.0):
+    """The same problem with its content queries scaled by `scale` (then
+    rounded to bf16): scores spread `scale` times wider, so the softmax sits
+    on a few tokens and near ties between them are common, and every score's
+    staging error grows by the same factor.  With fp16 c_hat alone in the
+    scores, such inputs reach about 3e-3 output and 5e-3 LSE error
+    (tests/test_precision_model.py); the bf8 residual correction keeps them
+    near 5e-4."""
+    q = oracle.bf16_bits_to_f64(prob.q_c_bits) * scale
+    prob.q_c_bits = workloads.to_bf16_bits(q.astype(np.float32))
+    return prob
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_decode_peaked_scores(heads):
+    prob = peaked(workloads.make_problem("v2lite_32k", ctx_lens=[700, 2100, 33, 5000], heads=heads, seed=77))
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    out, lse = run_decode(prob, device_cache_from(oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+    print(f"peaked scores, {heads} heads: out err {err:.2e}, lse err {lerr:.2e}")
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_decode_peaked_scores_protected(heads):
+    """Peaked scores with sink / recent BF16 rows among the decoded tokens."""
+    prob = peaked(workloads.make_problem("ragged_protect", ctx_lens=[90, 1300, 4100], heads=heads, seed=78))
+    oc, _ = oracle_cache_for(prob, z=z_of(prob))
+    ref_out, ref_lse = oracle_decode(prob, oc)
+    out, lse = run_decode(prob, device_cache_from(oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
+    print(f"peaked scores, protected, {heads} heads: out err {err:.2e}, lse err {lerr:.2e}")
 
 
 @pytest.mark.parametrize("heads", [16, 128])
@@ -94,7 +120,7 @@ def test_decode_rising_scores_rescale(heads):
     oc, _ = oracle_cache_for(prob, z=z_of(prob))
     ref_out, ref_lse = oracle_decode(prob, oc)
     out, lse = run_decode(prob, device_cache_from(oc))
-    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
     print(f"rising scores: out err {err:.2e}, lse err {lerr:.2e}")
 
 
@@ -104,7 +130,7 @@ def test_decode_empty_and_short_contexts(heads):
     oc, _ = oracle_cache_for(prob, z=z_of(prob))
     ref_out, ref_lse = oracle_decode(prob, oc)
     out, lse = run_decode(prob, device_cache_from(oc))
-    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
 
 
 @pytest.mark.parametrize("heads", [16, 128])
@@ -128,8 +154,8 @@ def test_decode_split_invariance():
     assert rlq.decode_workspace_size(2, 16, 120000) != rlq.decode_workspace_size(2, 16, 5000)
     out1, lse1 = run_decode(prob, dc)
     out2, lse2 = run_decode(prob, dc, max_ctx_len=120000)
-    check_decode(out1, lse1, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
-    check_decode(out2, lse2, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    check_decode(out1, lse1, ref_out, ref_lse, prob.ctx_lens)
+    check_decode(out2, lse2, ref_out, ref_lse, prob.ctx_lens)
     d = (out1 - out2).abs().amax(dim=-1) / out1.abs().amax(dim=-1)
     assert float(d.max()) < 1e-3
     assert float((lse1 - lse2).abs().max()) < 5e-4
@@ -181,7 +207,7 @@ def test_end_to_end_append_then_decode(case):
                         dev(prob.start_pos), dev(prob.block_table), latent=dev(prob.latent_bits),
                         rotation=dev(prob.rotation_bits))
     out, lse = run_decode(prob, dc)
-    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
 
 
 def test_decode_invalid_arguments():

@@ -2,8 +2,8 @@
 configurations bench.py times (same batch, heads and context lengths, so the
 same split grid or work-item plan).
 
-* 4 x 262,144-token decode, 16 heads: every output row and LSE against the
-  oracle.
+* 4 x 32,768- and 4 x 262,144-token decode, 16 heads: every output row and
+  LSE against the oracle.
 * 32-request ragged decode, 128 heads, 4 sink + 64 recent BF16 tokens,
   log-uniform lengths in [1,024, 65,536]: every output row and LSE.
 * 4 x 65,536-token bulk append through the bf16 MFMA rotation: z, group
@@ -25,7 +25,7 @@ import torch
 import oracle
 from decode_attention_rlq_amd import rlq, workloads
 from gpu_helpers import (check_decode, check_rotated_append, dev, device_cache_from, empty_device_cache,
-                         extend_lse_tolerance, lse_tolerance, oracle_cache_for, oracle_decode, params_of, run_decode)
+                         oracle_cache_for, oracle_decode, params_of, run_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def latents_as_z(prob):
     return (prob.latent_bits.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("name", ["v2lite_256k", "ragged_protect"])
+@pytest.mark.parametrize("name", ["v2lite_32k", "v2lite_256k", "ragged_protect"])
 def test_decode_full_size(name):
     prob = workloads.make_problem(name)
     print(f"{name}: batch {prob.batch}, heads {prob.heads}, tokens {int(prob.ctx_lens.sum())}", flush=True)
@@ -45,7 +45,7 @@ def test_decode_full_size(name):
     del dc
     torch.cuda.empty_cache()
     ref_out, ref_lse = oracle_decode(prob, oc)
-    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens, lse_tolerance(prob, oc))
+    err, lerr = check_decode(out, lse, ref_out, ref_lse, prob.ctx_lens)
     print(f"{name}: out err {err:.2e}, lse err {lerr:.2e}")
 
 
@@ -92,7 +92,6 @@ def test_extend_full_size_sampled():
             r, pos = b * chunk + i, n - chunk + i
             ref_o, ref_l = oracle.extend(oc, qc[r:r + 1], qr[r:r + 1], prob.sm_scale, view.block_table, [pos + 1],
                                          one, prob.gain, prob.level_inner, prob.level_outer)
-            tol = extend_lse_tolerance(view, oc, qc[r:r + 1], one, [pos + 1])
-            e = check_decode(out[r:r + 1], lse[r:r + 1], ref_o, ref_l, [1], tol)
+            e = check_decode(out[r:r + 1], lse[r:r + 1], ref_o, ref_l, [1])
             worst = [max(worst[0], e[0]), max(worst[1], e[1])]
     print(f"extend full size: sampled out err {worst[0]:.2e}, lse err {worst[1]:.2e}")

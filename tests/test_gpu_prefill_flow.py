@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from decode_attention_rlq_amd import rlq, workloads
-from gpu_helpers import check_decode, dev, extend_lse_tolerance, host_bits, lse_tolerance, params_of
+from gpu_helpers import check_decode, dev, host_bits, params_of
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,7 @@ def test_chunked_prefill_then_decode(heads):
                                   int(ctx.max()))
         torch.cuda.synchronize()
         rows_ctx = np.ones(total, np.int64)
-        e = check_decode(out, lse, ref_o, ref_l, rows_ctx, extend_lse_tolerance(prob, oc, qc, cu, ctx))
+        e = check_decode(out, lse, ref_o, ref_l, rows_ctx)
         worst = [max(worst[0], e[0]), max(worst[1], e[1])]
         compare_pools(dc, oc)
         done = [done[b] + n_new[b] for b in range(B)]
@@ -86,6 +86,6 @@ def test_chunked_prefill_then_decode(heads):
                                      prob.level_inner, prob.level_outer)
         out, lse = rlq.mla_decode(p, dc, q_c, q_r, prob.sm_scale, bt, dev(ctx), int(ctx.max()))
         torch.cuda.synchronize()
-        check_decode(out, lse, ref_o, ref_l, ctx, lse_tolerance(prob, oc, ctx))
+        check_decode(out, lse, ref_o, ref_l, ctx)
         cur = [c + 1 for c in cur]
     compare_pools(dc, oc)
