@@ -5,7 +5,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "rlq_internal.h"
+
+// Scratch of rlq_mla_decode_noalloc: one array per device, living as long as
+// the process.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device (with
+// that device current) and kept (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[RLQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -34,6 +42,27 @@ int check_device() {
     known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
   }
   return known[dev] == 1 ? RLQ_OK : RLQ_EUNSUPPORTED;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return RLQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || !aligned(p, 256)) return RLQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RLQ_OK;
 }
 
 int check_cache(const rlq_cache *c, int32_t batch) {
@@ -152,13 +181,16 @@ int rlq_mla_decode_workspace_size(int32_t batch, int32_t heads, int32_t max_ctx_
   return RLQ_OK;
 }
 
-int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
-                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
-                   int32_t batch, int32_t heads, float sm_scale,
-                   const int32_t *block_table, int32_t max_pages_per_req,
-                   const int32_t *ctx_lens, int32_t max_ctx_len,
-                   float *out, float *lse,
-                   void *workspace, size_t workspace_bytes, void *stream) {
+// The decode of rlq_mla_decode and rlq_mla_decode_noalloc.  With noalloc the
+// workspace is this library's static scratch array on the current device,
+// looked up only after every argument has been validated.
+static int decode_call(const rlq_layer_params *p, const rlq_cache *cache,
+                       const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                       int32_t batch, int32_t heads, float sm_scale,
+                       const int32_t *block_table, int32_t max_pages_per_req,
+                       const int32_t *ctx_lens, int32_t max_ctx_len,
+                       float *out, float *lse,
+                       void *workspace, size_t workspace_bytes, bool noalloc, void *stream) {
   if (p == nullptr || !decode_shape(batch, heads)) return RLQ_EINVAL;
   if (max_ctx_len < 0 || max_ctx_len > RLQ_MAX_CTX || max_pages_per_req < 1 ||
       (int64_t)max_ctx_len > (int64_t)max_pages_per_req * RLQ_PAGE)
@@ -166,10 +198,10 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   int st = check_cache(cache, batch);
   if (st != RLQ_OK) return st;
   if (q_c_bf16 == nullptr || q_r_bf16 == nullptr || block_table == nullptr ||
-      ctx_lens == nullptr || out == nullptr || workspace == nullptr)
+      ctx_lens == nullptr || out == nullptr || (!noalloc && workspace == nullptr))
     return RLQ_EINVAL;
   if (!aligned(q_c_bf16, 16) || !aligned(q_r_bf16, 16) || !aligned(out, 16) ||
-      !aligned(workspace, 16) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
+      (!noalloc && !aligned(workspace, 16)) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
       (lse != nullptr && !aligned(lse, 4)))
     return RLQ_EINVAL;
   const bool wide = rlq::use_wide(heads);
@@ -177,9 +209,14 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   const rlq::WidePlan wplan = rlq::plan_wide(batch, heads, max_ctx_len);
   const size_t need = wide ? rlq::wide_workspace_bytes(batch, heads, wplan)
                            : rlq::decode_workspace_bytes(batch, heads, plan);
+  if (noalloc) workspace_bytes = RLQ_NOALLOC_SCRATCH_BYTES;
   if (workspace_bytes < need) return RLQ_ENOSPC;
   st = check_device();
   if (st != RLQ_OK) return st;
+  if (noalloc) {
+    st = scratch_ptr(&workspace);
+    if (st != RLQ_OK) return st;
+  }
 
   rlq::DecodeArgs a;
   a.codes = cache->codes;
@@ -223,6 +260,27 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
   a.part_ml = a.part_o + parts * rlq::kPartialFloats;
   a.plan = nullptr;
   return hip_status(rlq::launch_decode(a, batch, (hipStream_t)stream));
+}
+
+int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
+                   const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                   int32_t batch, int32_t heads, float sm_scale,
+                   const int32_t *block_table, int32_t max_pages_per_req,
+                   const int32_t *ctx_lens, int32_t max_ctx_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_call(p, cache, q_c_bf16, q_r_bf16, batch, heads, sm_scale, block_table, max_pages_per_req,
+                     ctx_lens, max_ctx_len, out, lse, workspace, workspace_bytes, false, stream);
+}
+
+int rlq_mla_decode_noalloc(const rlq_layer_params *p, const rlq_cache *cache,
+                           const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                           int32_t batch, int32_t heads, float sm_scale,
+                           const int32_t *block_table, int32_t max_pages_per_req,
+                           const int32_t *ctx_lens, int32_t max_ctx_len,
+                           float *out, float *lse, void *stream) {
+  return decode_call(p, cache, q_c_bf16, q_r_bf16, batch, heads, sm_scale, block_table, max_pages_per_req,
+                     ctx_lens, max_ctx_len, out, lse, nullptr, 0, true, stream);
 }
 
 // Extend: the many-head kernel over (query, head) rows, the rows of the

@@ -22,8 +22,9 @@ DC, DR, GROUP, NGROUPS, PAGE, WORDS = 512, 64, 128, 4, 64, 32
 EXPORTED = (
     "rlq_abi_version", "rlq_layer_params_default", "rlq_status_string", "rlq_last_hip_error",
     "rlq_coupled_gain", "rlq_quantize_append", "rlq_mla_decode_workspace_size", "rlq_mla_decode",
-    "rlq_mla_extend_workspace_size", "rlq_mla_extend",
+    "rlq_mla_extend_workspace_size", "rlq_mla_extend", "rlq_mla_decode_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20   # RLQ_NOALLOC_SCRATCH_BYTES
 
 
 class LayerParams(ctypes.Structure):
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.rlq_mla_decode.argtypes = [
         ctypes.POINTER(LayerParams), ctypes.POINTER(CacheDesc), vp, vp, i32, i32, f32,
         vp, i32, vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    L.rlq_mla_decode_noalloc.restype = ctypes.c_int
+    L.rlq_mla_decode_noalloc.argtypes = [
+        ctypes.POINTER(LayerParams), ctypes.POINTER(CacheDesc), vp, vp, i32, i32, f32,
+        vp, i32, vp, i32, vp, vp, vp]
     L.rlq_mla_extend_workspace_size.restype = ctypes.c_int
     L.rlq_mla_extend_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.rlq_mla_extend.restype = ctypes.c_int
@@ -218,6 +223,28 @@ def mla_decode(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "rlq_mla_decode")
+    return out, lse
+
+
+def mla_decode_noalloc(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.Tensor,
+                       sm_scale: float, block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                       max_ctx_len: int, *, out: torch.Tensor, lse: torch.Tensor | None = None, stream=None):
+    """rlq_mla_decode_noalloc (see include/rlq.h): rlq_mla_decode with the
+    library's static scratch instead of a workspace; `out` (and `lse`) are
+    caller-allocated, so the call allocates nothing.  Returns (out, lse)."""
+    batch, heads = q_c.shape[0], q_c.shape[1]
+    desc = cache.desc()
+    st = lib().rlq_mla_decode_noalloc(
+        ctypes.byref(p), ctypes.byref(desc), _ptr(q_c, torch.bfloat16, "q_c"),
+        _ptr(q_r, torch.bfloat16, "q_r"), batch, heads, float(sm_scale),
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), int(max_ctx_len),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream))
+    if st == RLQ_ENOSPC:
+        need = decode_workspace_size(batch, heads, max_ctx_len)
+        raise RlqError(st, f"rlq_mla_decode_noalloc (needs {need} bytes of scratch, "
+                           f"the static array holds {NOALLOC_SCRATCH_BYTES})")
+    _check(st, "rlq_mla_decode_noalloc")
     return out, lse
 
 

@@ -31,9 +31,10 @@
  *    and owns them.  The library allocates nothing, keeps no pointer after a
  *    call returns and never synchronizes: work is enqueued on `stream` and the
  *    caller keeps every buffer alive until the stream has completed it.  Its
- *    only process-wide state is a per-device "is gfx950" check result and the
+ *    only process-wide state is a per-device "is gfx950" check result, the
  *    one-time LDS-size attributes of the decode and bulk-append kernels, all set
- *    on first use.
+ *    on first use, and the static scratch array of rlq_mla_decode_noalloc (one
+ *    per device, part of the loaded code object).
  *  - Device pointers must be 16-byte aligned and their arrays contiguous in
  *    the layouts given below.
  *  - Each call returns an RLQ_* status.  Host-side validation runs before any
@@ -76,6 +77,7 @@ enum {
 #define RLQ_WORDS 32      /* uint32 code words per token (16 codes per word)       */
 #define RLQ_MAX_HEADS 128
 #define RLQ_MAX_CTX 4194304  /* longest context one decode call accepts (tokens)  */
+#define RLQ_NOALLOC_SCRATCH_BYTES (64u << 20)  /* static scratch of rlq_mla_decode_noalloc */
 
 /*
  * Per-layer quantizer parameters, fixed while serving (§3.3).
@@ -238,6 +240,28 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
                    const int32_t *ctx_lens, int32_t max_ctx_len,
                    float *out, float *lse,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rlq_mla_decode_noalloc - rlq_mla_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and kernels, with the
+ * workspace taken from a static array of RLQ_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on each device it runs on until the process ends.
+ * Arguments as for rlq_mla_decode without workspace / workspace_bytes; the
+ * caller still passes the inputs and outputs.  Nothing is allocated: the
+ * array's device address is looked up once per device.
+ * Calls that overlap on one device (concurrent streams, or threads) share the
+ * array and race; serialize them.  The array needs no initialisation.
+ * Errors: as rlq_mla_decode; RLQ_ENOSPC when rlq_mla_decode_workspace_size()
+ * for these arguments exceeds RLQ_NOALLOC_SCRATCH_BYTES (e.g. batch 2 at
+ * RLQ_MAX_CTX with 128 heads needs 34 MB, which fits).
+ */
+int rlq_mla_decode_noalloc(const rlq_layer_params *p, const rlq_cache *cache,
+                           const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
+                           int32_t batch, int32_t heads, float sm_scale,
+                           const int32_t *block_table, int32_t max_pages_per_req,
+                           const int32_t *ctx_lens, int32_t max_ctx_len,
+                           float *out, float *lse, void *stream);
 
 /*
  * Workspace (bytes) that rlq_mla_extend needs: split partials for
