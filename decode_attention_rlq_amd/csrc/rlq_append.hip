@@ -461,13 +461,11 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(append_small_kernel, dim3((unsigned)blocks, RLQ_NGROUPS), dim3(64 * kSmallWaves), 0,
                        stream, a);
   } else {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)append_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kBulkLds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static PerDeviceOnce attr;
+    hipError_t ea = once_per_device(attr, [] {
+      return hipFuncSetAttribute((const void *)append_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kBulkLds);
+    });
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL(append_kernel, dim3(kBulkGrid), dim3(64 * kBulkWaves), kBulkLds, stream, a);
   }
   return hipGetLastError();

@@ -43,9 +43,9 @@ constexpr int kLdsBytes = kChatBytes + kXchBytes;      // 160 KB: one workgroup 
 constexpr int kResidentWorkgroups = 256;
 // Partial-score exchange between the two waves of a pair: an empty slot holds
 // this NaN pattern (no partial score of finite inputs is NaN); a reader polls
-// at most kSpinLimit times before going on.
+// at most A.spin_limit times, then gives up and marks the workgroup's partial
+// NaN, so the call's output and LSE for those rows come out NaN.
 constexpr uint32_t kPoison = 0x7fbadbadu;
-constexpr int kSpinLimit = 1 << 16;
 
 // What one lane loads for its tokens of a wave tile (32 consecutive tokens as
 // two 16-token sub-tiles), for the latent half h of its wave (K-steps 8h ..
@@ -225,8 +225,11 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   // Exchange slots of partial scores, [pair][parity][half][sub-tile][64 lanes].
   // A slot holding kPoison in any element is empty: the reader re-poisons a
   // slot after consuming it, so readiness needs no flag and no barrier.
-  f4 *xch = (f4 *)(smem + kChatBytes);
-  auto xch_at = [&](int i, int half) -> f4 * { return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64; };
+  // The slots are accessed as volatile: a store that publishes a partial and
+  // the partner's polling loads are not reordered or merged by the compiler.
+  volatile f4 *xch = (volatile f4 *)(smem + kChatBytes);
+  auto xch_at = [&](int i, int half) -> volatile f4 * { return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64; };
+  bool xch_lost = false;  // a poll gave up (wave-uniform)
   const f4 poison = __builtin_bit_cast(f4, u4{kPoison, kPoison, kPoison, kPoison});
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -368,13 +371,13 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     };
     half8 av0[4];
     f4 o0, o1;
-    f4 *other = xch_at(i - 1, h ^ 1);
+    volatile f4 *other = xch_at(i - 1, h ^ 1);
     if constexpr (kValue) {
       // This wave's partial of tile i-1, finished in the previous step, is
       // published now rather than at the end of that step, so no wave waits
       // there for its last MFMAs.  The partner does the same; its partial is
       // read here and consumed after part 1.
-      f4 *mine = xch_at(i - 1, h);
+      volatile f4 *mine = xch_at(i - 1, h);
       mine[lane] = acc_prev[0];
       mine[64 + lane] = acc_prev[1];
       o0 = other[lane];
@@ -383,16 +386,20 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     }
     if constexpr (kScore) score_pair(0);
     if constexpr (kValue) {
-      if (!slot_full(o0, o1)) {
+      bool ready = slot_full(o0, o1) && !A.force_xch_timeout;
+      if (!ready) {
         // Rare: the partner is behind.  Poll with a bound, so a wave can never
         // wait forever.
-        for (int n = 0; n < kSpinLimit; ++n) {
+        for (int n = 0; n < A.spin_limit; ++n) {
           __builtin_amdgcn_s_sleep(2);
-          asm volatile("" ::: "memory");
           o0 = other[lane];
           o1 = other[64 + lane];
-          if (slot_full(o0, o1)) break;
+          if (slot_full(o0, o1) && !A.force_xch_timeout) {
+            ready = true;
+            break;
+          }
         }
+        xch_lost |= !ready;
       }
       other[lane] = poison;
       other[64 + lane] = poison;
@@ -503,6 +510,8 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   l_run = sum_over_groups(l_run);
   __syncthreads();  // every wave is done with its c_hat region and the exchange
   float *ml = (float *)(smem + kChatBytes);  // [pair][16 heads][2]
+  int *lost = (int *)(ml + kPairs * 32);     // [wave]: a poll of this wave gave up
+  if (lane == 0) lost[wave] = xch_lost ? 1 : 0;
   if (pr > 0) {
     if (h == 0 && g4 == 0) {
       ml[(pr * 16 + r16) * 2] = m_run;
@@ -529,6 +538,10 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
       sc[v] = __builtin_amdgcn_exp2f(mv[v] - Mc);
       L += sc[v] * (v == 0 ? l_run : ml[(v * 16 + r16) * 2 + 1]);
     }
+    int any_lost = 0;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) any_lost |= lost[w];
+    if (any_lost) L = __builtin_nanf("");  // the merge turns it into NaN output and LSE
     const int64_t pidx = ((int64_t)b * HG + hg) * (A.splits + A.prot) + part;
     f4 *po = (f4 *)(A.part_o + pidx * kPartialFloats);
 #pragma unroll
@@ -610,14 +623,15 @@ size_t decode_workspace_bytes(int32_t batch, int32_t heads, const SplitPlan &pla
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static PerDeviceOnce attr;
+  hipError_t ea = once_per_device(attr, [] {
     for (const void *f : {(const void *)decode_split_kernel, (const void *)decode_prot_kernel}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return e;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (ea != hipSuccess) return ea;
   const int hg = a.heads / 16;
   if (a.prot) {
     hipLaunchKernelGGL(decode_prot_kernel, dim3(1, batch, hg), dim3(kDecodeThreads), kLdsBytes, stream, a);

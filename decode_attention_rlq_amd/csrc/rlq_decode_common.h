@@ -305,7 +305,9 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int64_t orow,
 #pragma unroll
     for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // L = 0: no tokens (out 0, lse -inf); L NaN: a split's partial is marked
+  // lost (out and lse NaN).
+  const float inv = L == 0.f ? 0.f : 1.f / L;
   float *o = A.out + (orow + hh) * RLQ_DC;
   for (int t = 0; t < njp; ++t) {
     const int jp = jp0 + t;
@@ -334,7 +336,7 @@ __device__ void merge_tiles(const DecodeArgs &A, int jp0, int njp, int64_t orow,
       for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
       if (A.lse != nullptr && jp == 0 && lane < 16)
         A.lse[orow + lane] =
-            L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+            L == 0.f ? kNegInf : (Mh + log2f(L) - kBias) * 0.69314718055994531f;
     }
     if (t + 1 < njp) __syncthreads();  // part is rewritten by the next tile
   }
@@ -409,7 +411,9 @@ __device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int64_t
   for (int i = 0; i < 16; ++i) L += red_l[i][hh];
 #pragma unroll
   for (int i = 0; i < 16; ++i) Mh = fmaxf(Mh, red_m[i][hh]);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // L = 0: no tokens (out 0, lse -inf); L NaN: a split's partial is marked
+  // lost (out and lse NaN).
+  const float inv = L == 0.f ? 0.f : 1.f / L;
   float *o = A.out + (orow + hh) * RLQ_DC;
   for (int t = grp; t < njp; t += kMergeWaves) {
     const int jp = jp0 + t;
@@ -418,7 +422,7 @@ __device__ void merge_tiles_multi(const DecodeArgs &A, int jp0, int njp, int64_t
     for (int i = 0; i < 4; ++i) o[value_coord(jp, 4 * (lane >> 4) + i)] = sum[i] * inv;
   }
   if (A.lse != nullptr && jp0 == 0 && tid < 16)
-    A.lse[orow + tid] = L > 0.f ? (Mh + log2f(L) - kBias) * 0.69314718055994531f : kNegInf;
+    A.lse[orow + tid] = L == 0.f ? kNegInf : (Mh + log2f(L) - kBias) * 0.69314718055994531f;
 }
 
 }  // namespace

@@ -636,14 +636,15 @@ size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan) 
 }
 
 hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static PerDeviceOnce attr;
+  hipError_t ea = once_per_device(attr, [] {
     for (const void *f : {(const void *)decode_wide_kernel<false>, (const void *)decode_wide_kernel<true>}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
       if (e != hipSuccess) return e;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (ea != hipSuccess) return ea;
   const dim3 grid(a.item_slots, a.heads / kWideHeads);
   if (a.prot)
     hipLaunchKernelGGL(decode_wide_kernel<true>, grid, dim3(kDecodeThreads), kWideLds, stream, a);

@@ -3,9 +3,11 @@
 
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "rlq_internal.h"
 
@@ -65,6 +67,33 @@ int scratch_ptr(void **ptr) {
   return RLQ_OK;
 }
 
+// Opt-in checks of the values that live in device memory (RLQ_DEBUG set to
+// anything but "0"): the call copies them to the host (synchronizing its
+// stream) and returns RLQ_EINVAL if one is out of range, before any launch.
+bool debug_checks() {
+  const char *e = getenv("RLQ_DEBUG");
+  return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+}
+
+// Test switch of the 16-head kernel's bounded exchange wait
+// (RLQ_TEST_EXCHANGE_TIMEOUT set to anything but "0"): every poll finds its
+// slot empty and gives up after two tries, so each workgroup marks its
+// partial lost and the call's outputs and LSE come out NaN.  Every kernel
+// still runs to its end.
+bool force_exchange_timeout() {
+  const char *e = getenv("RLQ_TEST_EXCHANGE_TIMEOUT");
+  return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+}
+
+// Copies `n` int32 of device memory to `host` in stream order.
+int fetch_i32(const int32_t *dev, size_t n, std::vector<int32_t> &host, hipStream_t stream) {
+  host.resize(n);
+  if (n == 0) return RLQ_OK;
+  hipError_t e = hipMemcpyAsync(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e);
+}
+
 int check_cache(const rlq_cache *c, int32_t batch) {
   if (c == nullptr || c->codes == nullptr || c->meta == nullptr || c->rope == nullptr)
     return RLQ_EINVAL;
@@ -118,6 +147,60 @@ float rlq_coupled_gain(float tau, float level_inner, float level_outer) {
   return (float)(1.0 / resp);
 }
 
+// Page ids of positions [p0, p1) of one request.
+static bool pages_ok(const int32_t *row, int64_t p0, int64_t p1, int32_t max_pages, int32_t num_pages) {
+  if (p1 <= p0) return true;
+  const int64_t first = p0 / RLQ_PAGE, last = (p1 - 1) / RLQ_PAGE;
+  if (p0 < 0 || last >= max_pages) return false;
+  for (int64_t i = first; i <= last; ++i)
+    if (row[i] < 0 || row[i] >= num_pages) return false;
+  return true;
+}
+
+int rlq_check_decode_tables(int32_t batch, const int32_t *ctx_lens, const int32_t *block_table,
+                            int32_t max_pages_per_req, int32_t num_pages, int32_t max_ctx_len) {
+  if (batch < 1 || ctx_lens == nullptr || block_table == nullptr || max_pages_per_req < 1 || num_pages < 1)
+    return RLQ_EINVAL;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = ctx_lens[b];
+    if (n < 0 || n > max_ctx_len) return RLQ_EINVAL;
+    if (!pages_ok(block_table + (int64_t)b * max_pages_per_req, 0, n, max_pages_per_req, num_pages))
+      return RLQ_EINVAL;
+  }
+  return RLQ_OK;
+}
+
+int rlq_check_append_tables(int32_t batch, const int32_t *cu_seqlens, const int32_t *start_pos,
+                            const int32_t *block_table, int32_t max_pages_per_req, int32_t num_pages,
+                            int64_t n_tokens) {
+  if (batch < 1 || cu_seqlens == nullptr || start_pos == nullptr || block_table == nullptr ||
+      max_pages_per_req < 1 || num_pages < 1)
+    return RLQ_EINVAL;
+  if (cu_seqlens[0] != 0 || cu_seqlens[batch] != n_tokens) return RLQ_EINVAL;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n < 0 || start_pos[b] < 0) return RLQ_EINVAL;
+    if (!pages_ok(block_table + (int64_t)b * max_pages_per_req, start_pos[b], start_pos[b] + n,
+                  max_pages_per_req, num_pages))
+      return RLQ_EINVAL;
+  }
+  return RLQ_OK;
+}
+
+int rlq_check_extend_tables(int32_t batch, const int32_t *cu_seqlens_q, const int32_t *ctx_lens,
+                            const int32_t *block_table, int32_t max_pages_per_req, int32_t num_pages,
+                            int32_t max_q_len, int32_t max_ctx_len) {
+  if (cu_seqlens_q == nullptr) return RLQ_EINVAL;
+  const int st = rlq_check_decode_tables(batch, ctx_lens, block_table, max_pages_per_req, num_pages, max_ctx_len);
+  if (st != RLQ_OK) return st;
+  if (cu_seqlens_q[0] != 0) return RLQ_EINVAL;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t nq = (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+    if (nq < 0 || nq > max_q_len || nq > ctx_lens[b]) return RLQ_EINVAL;
+  }
+  return RLQ_OK;
+}
+
 int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
                         const uint16_t *latent_bf16, const float *latent_rot_f32,
                         const uint16_t *rotation_bf16, const uint16_t *k_rope_bf16,
@@ -139,6 +222,16 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
   if (z_debug != nullptr && !aligned(z_debug, 16)) return RLQ_EINVAL;
   st = check_device();
   if (st != RLQ_OK) return st;
+  if (debug_checks()) {
+    std::vector<int32_t> cu, sp, bt;
+    if ((st = fetch_i32(cu_seqlens, (size_t)batch + 1, cu, (hipStream_t)stream)) != RLQ_OK) return st;
+    if ((st = fetch_i32(start_pos, (size_t)batch, sp, (hipStream_t)stream)) != RLQ_OK) return st;
+    if ((st = fetch_i32(block_table, (size_t)batch * max_pages_per_req, bt, (hipStream_t)stream)) != RLQ_OK)
+      return st;
+    st = rlq_check_append_tables(batch, cu.data(), sp.data(), bt.data(), max_pages_per_req, cache->num_pages,
+                                 n_tokens);
+    if (st != RLQ_OK) return st;
+  }
   if (n_tokens == 0) return RLQ_OK;
 
   rlq::AppendArgs a;
@@ -213,6 +306,14 @@ static int decode_call(const rlq_layer_params *p, const rlq_cache *cache,
   if (workspace_bytes < need) return RLQ_ENOSPC;
   st = check_device();
   if (st != RLQ_OK) return st;
+  if (debug_checks()) {
+    std::vector<int32_t> cl, bt;
+    if ((st = fetch_i32(ctx_lens, (size_t)batch, cl, (hipStream_t)stream)) != RLQ_OK) return st;
+    if ((st = fetch_i32(block_table, (size_t)batch * max_pages_per_req, bt, (hipStream_t)stream)) != RLQ_OK)
+      return st;
+    st = rlq_check_decode_tables(batch, cl.data(), bt.data(), max_pages_per_req, cache->num_pages, max_ctx_len);
+    if (st != RLQ_OK) return st;
+  }
   if (noalloc) {
     st = scratch_ptr(&workspace);
     if (st != RLQ_OK) return st;
@@ -247,6 +348,8 @@ static int decode_call(const rlq_layer_params *p, const rlq_cache *cache,
   a.item_target = wplan.item_target;
   a.cu_q = nullptr;
   a.q_heads = heads;
+  a.force_xch_timeout = force_exchange_timeout() ? 1 : 0;
+  a.spin_limit = a.force_xch_timeout ? 2 : (1 << 16);
   if (wide) {
     // Many heads: balanced work items, each 32-token tile decoded once per 64 heads.
     const size_t parts = (size_t)wplan.item_slots * (heads / 16);
@@ -327,6 +430,16 @@ int rlq_mla_extend(const rlq_layer_params *p, const rlq_cache *cache,
   if (workspace_bytes < rlq::wide_workspace_bytes(batch, (int32_t)rows, wplan)) return RLQ_ENOSPC;
   st = check_device();
   if (st != RLQ_OK) return st;
+  if (debug_checks()) {
+    std::vector<int32_t> cq, cl, bt;
+    if ((st = fetch_i32(cu_seqlens_q, (size_t)batch + 1, cq, (hipStream_t)stream)) != RLQ_OK) return st;
+    if ((st = fetch_i32(ctx_lens, (size_t)batch, cl, (hipStream_t)stream)) != RLQ_OK) return st;
+    if ((st = fetch_i32(block_table, (size_t)batch * max_pages_per_req, bt, (hipStream_t)stream)) != RLQ_OK)
+      return st;
+    st = rlq_check_extend_tables(batch, cq.data(), cl.data(), bt.data(), max_pages_per_req, cache->num_pages,
+                                 max_q_len, max_ctx_len);
+    if (st != RLQ_OK) return st;
+  }
 
   rlq::DecodeArgs a;
   a.codes = cache->codes;
@@ -357,6 +470,8 @@ int rlq_mla_extend(const rlq_layer_params *p, const rlq_cache *cache,
   a.item_target = wplan.item_target;
   a.cu_q = cu_seqlens_q;
   a.q_heads = heads;
+  a.force_xch_timeout = 0;
+  a.spin_limit = 1 << 16;
   const size_t parts = (size_t)wplan.item_slots * (size_t)(rows / 16);
   a.part_o = (float *)workspace;
   a.part_ml = a.part_o + parts * rlq::kPartialFloats;

@@ -4,9 +4,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "rlq.h"
 
 namespace rlq {
+
+// A one-time set-up step (a kernel attribute) run once per device, safe when
+// several host threads launch at once.
+struct PerDeviceOnce {
+  std::mutex m;
+  bool done[64] = {};
+};
+template <class F>
+hipError_t once_per_device(PerDeviceOnce &o, F &&f) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(o.m);
+  if (!o.done[dev]) {
+    e = f();
+    if (e != hipSuccess) return e;
+    o.done[dev] = true;
+  }
+  return hipSuccess;
+}
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -94,6 +117,11 @@ struct DecodeArgs {
   // largest request (a multiple of 64).
   const int32_t *cu_q;
   int32_t q_heads;
+  // Bounded wait of the 16-head kernel's partial-score exchange: polls before
+  // a wave gives up (and marks its partial NaN), and a test switch that makes
+  // every poll find its slot empty.
+  int32_t spin_limit;
+  int32_t force_xch_timeout;
 };
 
 // Split policy shared by the workspace query and the launch.

@@ -23,6 +23,7 @@ EXPORTED = (
     "rlq_abi_version", "rlq_layer_params_default", "rlq_status_string", "rlq_last_hip_error",
     "rlq_coupled_gain", "rlq_quantize_append", "rlq_mla_decode_workspace_size", "rlq_mla_decode",
     "rlq_mla_extend_workspace_size", "rlq_mla_extend", "rlq_mla_decode_noalloc",
+    "rlq_check_decode_tables", "rlq_check_append_tables", "rlq_check_extend_tables",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20   # RLQ_NOALLOC_SCRATCH_BYTES
 
@@ -77,6 +78,11 @@ def lib() -> ctypes.CDLL:
     L.rlq_mla_decode_noalloc.argtypes = [
         ctypes.POINTER(LayerParams), ctypes.POINTER(CacheDesc), vp, vp, i32, i32, f32,
         vp, i32, vp, i32, vp, vp, vp]
+    for name, extra in (("rlq_check_decode_tables", [i32, vp, vp, i32, i32, i32]),
+                        ("rlq_check_append_tables", [i32, vp, vp, vp, i32, i32, i64]),
+                        ("rlq_check_extend_tables", [i32, vp, vp, vp, i32, i32, i32, i32])):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = extra
     L.rlq_mla_extend_workspace_size.restype = ctypes.c_int
     L.rlq_mla_extend_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.rlq_mla_extend.restype = ctypes.c_int
@@ -113,6 +119,55 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None, name: str = "
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _shape(t: torch.Tensor | None, shape: tuple, name: str):
+    """Raise ValueError unless t has `shape` (None entries match any size)."""
+    if t is None:
+        return
+    ok = t.dim() == len(shape) and all(w is None or int(d) == w for d, w in zip(t.shape, shape))
+    if not ok:
+        want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+        raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+
+
+def _rows_at_least(t: torch.Tensor, rows: int, name: str):
+    if t.dim() != 2 or t.shape[0] < rows:
+        raise ValueError(f"{name} must be 2-D with at least {rows} rows, got {list(t.shape)}")
+
+
+def _i32_host(a) -> ctypes.c_void_p:
+    import numpy as np
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def check_decode_tables(ctx_lens, block_table, num_pages: int, max_ctx_len: int) -> int:
+    """rlq_check_decode_tables on host arrays; returns the RLQ_* status."""
+    cl, pc = _i32_host(ctx_lens)
+    bt, pb = _i32_host(block_table)
+    return lib().rlq_check_decode_tables(len(cl), pc, pb, bt.shape[1], num_pages, max_ctx_len)
+
+
+def check_append_tables(cu_seqlens, start_pos, block_table, num_pages: int, n_tokens: int) -> int:
+    """rlq_check_append_tables on host arrays; returns the RLQ_* status."""
+    cu, pc = _i32_host(cu_seqlens)
+    sp, ps = _i32_host(start_pos)
+    bt, pb = _i32_host(block_table)
+    if len(cu) != len(sp) + 1:
+        return RLQ_EINVAL
+    return lib().rlq_check_append_tables(len(sp), pc, ps, pb, bt.shape[1], num_pages, n_tokens)
+
+
+def check_extend_tables(cu_seqlens_q, ctx_lens, block_table, num_pages: int, max_q_len: int,
+                        max_ctx_len: int) -> int:
+    """rlq_check_extend_tables on host arrays; returns the RLQ_* status."""
+    cq, pq = _i32_host(cu_seqlens_q)
+    cl, pc = _i32_host(ctx_lens)
+    bt, pb = _i32_host(block_table)
+    if len(cq) != len(cl) + 1:
+        return RLQ_EINVAL
+    return lib().rlq_check_extend_tables(len(cl), pq, pc, pb, bt.shape[1], num_pages, max_q_len, max_ctx_len)
 
 
 def _stream(stream) -> int:
@@ -162,6 +217,13 @@ class PagedCache:
         return self.codes.shape[0]
 
     def desc(self) -> CacheDesc:
+        _shape(self.codes, (None, PAGE, WORDS), "codes")
+        _shape(self.meta, (self.num_pages, PAGE, 2 * NGROUPS), "meta")
+        _shape(self.rope, (self.num_pages, PAGE, DR), "rope")
+        _shape(self.sink, (None, None, DC), "sink")
+        _shape(self.recent, (None, None, DC), "recent")
+        if self.sink is not None and self.recent is not None and self.sink.shape[0] != self.recent.shape[0]:
+            raise ValueError("sink and recent must have the same max_batch")
         mb = 0
         for t in (self.sink, self.recent):
             if t is not None:
@@ -182,6 +244,17 @@ def quantize_append(p: LayerParams, cache: PagedCache, k_rope: torch.Tensor,
     """rlq_quantize_append (see include/rlq.h)."""
     if n_tokens is None:
         n_tokens = k_rope.shape[0]
+    n, batch = int(n_tokens), start_pos.shape[0] if start_pos.dim() == 1 else -1
+    _shape(start_pos, (None,), "start_pos")
+    _shape(cu_seqlens, (batch + 1,), "cu_seqlens")
+    _rows_at_least(block_table, batch, "block_table")
+    # Token arrays hold at least n_tokens rows (the call reads the first n_tokens).
+    for t, w, name in ((k_rope, DR, "k_rope"), (latent, DC, "latent"), (latent_rot, DC, "latent_rot"),
+                       (z_debug, DC, "z_debug")):
+        if t is not None:
+            _shape(t, (None, w), name)
+            _rows_at_least(t, n, name)
+    _shape(rotation, (DC, DC), "rotation")
     desc = cache.desc()
     st = lib().rlq_quantize_append(
         ctypes.byref(p), ctypes.byref(desc), _ptr(latent, torch.bfloat16, "latent"),
@@ -200,12 +273,26 @@ def decode_workspace_size(batch: int, heads: int, max_ctx_len: int) -> int:
     return n.value
 
 
+def _decode_shapes(q_c, q_r, block_table, ctx_lens, out, lse):
+    """Shapes of a decode call's tensors; returns (batch, heads)."""
+    if q_c.dim() != 3:
+        raise ValueError(f"q_c must have shape [batch, heads, {DC}], got {list(q_c.shape)}")
+    batch, heads = int(q_c.shape[0]), int(q_c.shape[1])
+    _shape(q_c, (batch, heads, DC), "q_c")
+    _shape(q_r, (batch, heads, DR), "q_r")
+    _shape(ctx_lens, (batch,), "ctx_lens")
+    _rows_at_least(block_table, batch, "block_table")
+    _shape(out, (batch, heads, DC), "out")
+    _shape(lse, (batch, heads), "lse")
+    return batch, heads
+
+
 def mla_decode(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.Tensor,
                sm_scale: float, block_table: torch.Tensor, ctx_lens: torch.Tensor,
                max_ctx_len: int, *, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                want_lse: bool = True, workspace: torch.Tensor | None = None, stream=None):
     """rlq_mla_decode (see include/rlq.h).  Returns (out, lse)."""
-    batch, heads = q_c.shape[0], q_c.shape[1]
+    batch, heads = _decode_shapes(q_c, q_r, block_table, ctx_lens, out, lse)
     if out is None:
         out = torch.empty((batch, heads, DC), dtype=torch.float32, device=q_c.device)
     if lse is None and want_lse:
@@ -232,7 +319,7 @@ def mla_decode_noalloc(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r
     """rlq_mla_decode_noalloc (see include/rlq.h): rlq_mla_decode with the
     library's static scratch instead of a workspace; `out` (and `lse`) are
     caller-allocated, so the call allocates nothing.  Returns (out, lse)."""
-    batch, heads = q_c.shape[0], q_c.shape[1]
+    batch, heads = _decode_shapes(q_c, q_r, block_table, ctx_lens, out, lse)
     desc = cache.desc()
     st = lib().rlq_mla_decode_noalloc(
         ctypes.byref(p), ctypes.byref(desc), _ptr(q_c, torch.bfloat16, "q_c"),
@@ -261,8 +348,16 @@ def mla_extend(p: LayerParams, cache: PagedCache, q_c: torch.Tensor, q_r: torch.
                lse: torch.Tensor | None = None, want_lse: bool = True,
                workspace: torch.Tensor | None = None, stream=None):
     """rlq_mla_extend (see include/rlq.h): q_c [total_q][heads][512].  Returns (out, lse)."""
-    total_q, heads = q_c.shape[0], q_c.shape[1]
+    if q_c.dim() != 3 or cu_seqlens_q.dim() != 1:
+        raise ValueError("q_c must be [total_q, heads, 512] and cu_seqlens_q 1-D")
+    total_q, heads = int(q_c.shape[0]), int(q_c.shape[1])
     batch = cu_seqlens_q.shape[0] - 1
+    _shape(q_c, (total_q, heads, DC), "q_c")
+    _shape(q_r, (total_q, heads, DR), "q_r")
+    _shape(ctx_lens, (batch,), "ctx_lens")
+    _rows_at_least(block_table, batch, "block_table")
+    _shape(out, (total_q, heads, DC), "out")
+    _shape(lse, (total_q, heads), "lse")
     if out is None:
         out = torch.empty((total_q, heads, DC), dtype=torch.float32, device=q_c.device)
     if lse is None and want_lse:

@@ -41,7 +41,17 @@
  *    launch; on error nothing is enqueued.  A launch failure reported by the
  *    HIP runtime returns RLQ_EHIP (text via rlq_last_hip_error()).
  *  - Values that live in device memory (block tables, lengths, positions) are
- *    trusted: out-of-range entries are undefined behaviour.
+ *    trusted: out-of-range entries are undefined behaviour.  With the
+ *    environment variable RLQ_DEBUG set (to anything but "0"), the decode,
+ *    extend and append calls first copy them to the host (synchronizing their
+ *    stream, so not under graph capture) and return RLQ_EINVAL, with nothing
+ *    launched, if one is out of range (the rlq_check_*_tables rules below).
+ *  - The 16-head decode kernel's two waves of a pair exchange partial scores
+ *    through LDS with a bounded wait; a wave that gives up (which needs a
+ *    partner stalled for milliseconds) marks its workgroup's partial, and the
+ *    affected rows of out and lse come out NaN instead of a silently wrong
+ *    value.  RLQ_TEST_EXCHANGE_TIMEOUT (anything but "0") forces that path
+ *    for tests; every kernel still completes.
  *  - Calls on one stream run in order; calls that overlap on different
  *    streams must not write the same cache slots.
  *  - Values: content latents must stay within the fp16 range (|x| < 65504);
@@ -144,6 +154,30 @@ const char *rlq_last_hip_error(void);
  * Host-only helper; returns NaN for non-positive levels.
  */
 float rlq_coupled_gain(float tau, float level_inner, float level_outer);
+
+/*
+ * Host-side checks of the device-resident tables, on host copies of them
+ * (the RLQ_DEBUG checks; callers may also use them directly).  Each returns
+ * RLQ_OK or RLQ_EINVAL.
+ *   rlq_check_decode_tables   every 0 <= ctx_lens[b] <= max_ctx_len, and the
+ *                             page ids of positions 0 .. ctx_lens[b]-1 lie in
+ *                             [0, num_pages) within max_pages_per_req columns
+ *   rlq_check_append_tables   cu_seqlens[0] = 0, non-decreasing, cu_seqlens
+ *                             [batch] = n_tokens; start_pos[b] >= 0; the page
+ *                             ids of the new positions in range as above
+ *   rlq_check_extend_tables   the decode rules, cu_seqlens_q[0] = 0 and every
+ *                             0 <= n_q <= min(max_q_len, ctx_lens[b])
+ * Arrays: ctx_lens, start_pos [batch]; cu_seqlens, cu_seqlens_q [batch+1];
+ * block_table [batch][max_pages_per_req] (host memory).
+ */
+int rlq_check_decode_tables(int32_t batch, const int32_t *ctx_lens, const int32_t *block_table,
+                            int32_t max_pages_per_req, int32_t num_pages, int32_t max_ctx_len);
+int rlq_check_append_tables(int32_t batch, const int32_t *cu_seqlens, const int32_t *start_pos,
+                            const int32_t *block_table, int32_t max_pages_per_req, int32_t num_pages,
+                            int64_t n_tokens);
+int rlq_check_extend_tables(int32_t batch, const int32_t *cu_seqlens_q, const int32_t *ctx_lens,
+                            const int32_t *block_table, int32_t max_pages_per_req, int32_t num_pages,
+                            int32_t max_q_len, int32_t max_ctx_len);
 
 /*
  * rlq_quantize_append - append new tokens of `batch` requests to the cache.

@@ -10,6 +10,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -171,3 +172,103 @@ def test_extend_workspace_and_validation(lib):
     assert E(*args(fake, 16, 65, 64, 1 << 30)) == -1  # more queries than context
     assert E(*args(fake, 16, 4, 257, 1 << 30)) == -1  # context beyond the block table
     assert E(*args(fake, 16, 4, 64, 16)) == -3        # workspace too small
+
+
+def test_check_decode_tables(lib):
+    ok, bad = rlq.RLQ_OK, rlq.RLQ_EINVAL
+    bt = np.array([[3, 1, 7, 7], [0, 2, 5, 9]], np.int32)  # column 3 of request 1 (9) is unused
+    assert rlq.check_decode_tables([129, 150], bt, 8, 256) == ok
+    assert rlq.check_decode_tables([0, 0], bt, 8, 0) == ok
+    assert rlq.check_decode_tables([129, 257], bt, 8, 256) == bad      # beyond max_ctx_len
+    assert rlq.check_decode_tables([-1, 64], bt, 8, 256) == bad        # negative length
+    assert rlq.check_decode_tables([129, 193], bt, 8, 256) == bad      # reaches page id 9 >= 8
+    assert rlq.check_decode_tables([129, 150], bt, 7, 256) == bad      # page id 7 >= 7
+    neg = bt.copy()
+    neg[0, 1] = -4
+    assert rlq.check_decode_tables([129, 150], neg, 8, 256) == bad
+    assert rlq.check_decode_tables([65, 150], neg, 8, 256) == bad
+    assert rlq.check_decode_tables([64, 150], neg, 8, 256) == ok       # page 1 not reached
+    assert rlq.check_decode_tables([300, 10], bt, 8, 300) == bad       # more pages than columns
+
+
+def test_check_append_tables(lib):
+    ok, bad = rlq.RLQ_OK, rlq.RLQ_EINVAL
+    bt = np.array([[0, 1], [2, 3]], np.int32)
+    assert rlq.check_append_tables([0, 10, 30], [60, 0], bt, 4, 30) == ok
+    assert rlq.check_append_tables([0, 0, 0], [0, 0], bt, 4, 0) == ok
+    assert rlq.check_append_tables([1, 10, 30], [60, 0], bt, 4, 30) == bad   # cu_seqlens[0] != 0
+    assert rlq.check_append_tables([0, 10, 9], [0, 0], bt, 4, 9) == bad      # decreasing
+    assert rlq.check_append_tables([0, 10, 30], [0, 0], bt, 4, 31) == bad    # total != n_tokens
+    assert rlq.check_append_tables([0, 10, 30], [-1, 0], bt, 4, 30) == bad   # negative start
+    assert rlq.check_append_tables([0, 10, 30], [120, 0], bt, 4, 30) == bad  # past the last column
+    assert rlq.check_append_tables([0, 10, 80], [60, 0], bt, 4, 80) == ok
+    assert rlq.check_append_tables([0, 10, 80], [60, 0], bt, 3, 80) == bad   # reaches page id 3 >= 3
+    assert rlq.check_append_tables([0, 10], [60, 0], bt, 4, 10) == bad       # cu_seqlens too short
+
+
+def test_check_extend_tables(lib):
+    ok, bad = rlq.RLQ_OK, rlq.RLQ_EINVAL
+    bt = np.array([[0, 1], [2, 3]], np.int32)
+    assert rlq.check_extend_tables([0, 5, 9], [100, 4], bt, 4, 5, 128) == ok
+    assert rlq.check_extend_tables([0, 0, 4], [100, 4], bt, 4, 5, 128) == ok
+    assert rlq.check_extend_tables([0, 5, 10], [100, 4], bt, 4, 5, 128) == bad  # 5 queries > ctx 4
+    assert rlq.check_extend_tables([0, 6, 9], [100, 4], bt, 4, 5, 128) == bad   # above max_q_len
+    assert rlq.check_extend_tables([1, 5, 9], [100, 4], bt, 4, 5, 128) == bad   # cu_seqlens_q[0] != 0
+    assert rlq.check_extend_tables([0, 5, 3], [100, 4], bt, 4, 5, 128) == bad   # negative count
+    assert rlq.check_extend_tables([0, 5, 9], [100, 4], bt, 4, 5, 99) == bad    # ctx above max_ctx_len
+
+
+def test_binding_rejects_misshaped_tensors(lib):
+    """Shape checks run in the binding before any device call (these tensors
+    live on the host: a well-shaped call would fail only on the device
+    check)."""
+    p = rlq.default_params()
+    cache = rlq.PagedCache.allocate(4, device="cpu")
+    B, H = 2, 16
+    q = torch.zeros((B, H, 512), dtype=torch.bfloat16)
+    qr = torch.zeros((B, H, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((B, 4), dtype=torch.int32)
+    ctx = torch.zeros(B, dtype=torch.int32)
+
+    def raises_shape(fn, what):
+        with pytest.raises(ValueError) as e:
+            fn()
+        assert "shape" in str(e.value) or "rows" in str(e.value), str(e.value)
+        assert what in str(e.value), str(e.value)
+
+    raises_shape(lambda: rlq.mla_decode(p, cache, q, qr[:, :8], 0.1, bt, ctx, 256), "q_r")
+    raises_shape(lambda: rlq.mla_decode(p, cache, q, qr, 0.1, bt, ctx[:1], 256), "ctx_lens")
+    raises_shape(lambda: rlq.mla_decode(p, cache, q, qr, 0.1, bt[:1], ctx, 256), "block_table")
+    raises_shape(lambda: rlq.mla_decode(p, cache, q, qr, 0.1, bt, ctx, 256,
+                                        out=torch.zeros((B, H, 256))), "out")
+    raises_shape(lambda: rlq.mla_decode(p, cache, q, qr, 0.1, bt, ctx, 256,
+                                        lse=torch.zeros((B, 2 * H))), "lse")
+    raises_shape(lambda: rlq.mla_decode(p, cache, q[..., :256], qr, 0.1, bt, ctx, 256), "q_c")
+    raises_shape(lambda: rlq.mla_decode_noalloc(p, cache, q, qr, 0.1, bt, ctx, 256,
+                                                out=torch.zeros((B + 1, H, 512))), "out")
+    cuq = torch.tensor([0, 3, 5], dtype=torch.int32)
+    raises_shape(lambda: rlq.mla_extend(p, cache, q[:1].expand(5, H, 512).contiguous(), qr, cuq, 3, 0.1,
+                                        bt, ctx, 256), "q_r")
+    raises_shape(lambda: rlq.mla_extend(p, cache, torch.zeros((5, H, 512), dtype=torch.bfloat16),
+                                        torch.zeros((5, H, 64), dtype=torch.bfloat16), cuq, 3, 0.1,
+                                        bt, ctx[:1], 256), "ctx_lens")
+    n = 10
+    kr = torch.zeros((n, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, n], dtype=torch.int32)
+    sp = torch.zeros(B, dtype=torch.int32)
+    raises_shape(lambda: rlq.quantize_append(p, cache, kr, cu, sp, bt,
+                                             latent_rot=torch.zeros((n - 1, 512))), "latent_rot")
+    raises_shape(lambda: rlq.quantize_append(p, cache, kr, cu, sp, bt,
+                                             latent_rot=torch.zeros((n, 256))), "latent_rot")
+    raises_shape(lambda: rlq.quantize_append(p, cache, kr[:4], cu, sp, bt, n_tokens=n,
+                                             latent_rot=torch.zeros((n, 512))), "k_rope")
+    raises_shape(lambda: rlq.quantize_append(p, cache, kr, cu[:2], sp, bt,
+                                             latent_rot=torch.zeros((n, 512))), "cu_seqlens")
+    raises_shape(lambda: rlq.quantize_append(p, cache, kr, cu, sp, bt, latent=torch.zeros((n, 512)),
+                                             rotation=torch.zeros((512, 256))), "rotation")
+    bad_cache = rlq.PagedCache(codes=cache.codes, meta=cache.meta[:, :, :4], rope=cache.rope)
+    raises_shape(lambda: rlq.mla_decode(p, bad_cache, q, qr, 0.1, bt, ctx, 256), "meta")
+    # A well-shaped call gets as far as the device check.
+    with pytest.raises(ValueError) as e:
+        rlq.mla_decode(p, cache, q, qr, 0.1, bt, ctx, 256)
+    assert "device tensor" in str(e.value)
