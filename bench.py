@@ -134,6 +134,98 @@ def copy_peak_gbps(torch, mib=1024, reps=5):
     return 2.0 * n / min(ts) / 1e9
 
 
+def per_call_us(torch, stream, fn, n):
+    """fn(0) .. fn(n-1), each bracketed by its own pair of HIP events on
+    `stream`; returns (median, p10, p90) of the per-call times in us."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+# --------------------------------------------------------------------------- measured ceilings
+
+def ceilings_lib():
+    import ctypes
+    path = os.path.join(ROOT, "decode_attention_rlq_amd", "librlq_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with `python -m decode_attention_rlq_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.rlq_ceiling_read.argtypes = [i32, vp, i64, vp, i32, vp]
+    L.rlq_ceiling_mfma.argtypes = [i32, i32, i32, vp, vp, vp]
+    L.rlq_ceiling_lds.argtypes = [i32, i32, i32, vp, vp]
+    return L
+
+
+def read_peak_gbps(torch, mib=1024, reps=5):
+    """HBM read-only streaming rate with 16-byte loads (a HIP kernel reading
+    `mib` MiB once per call; best of `reps` for each of a few grid sizes)."""
+    L = ceilings_lib()
+    n = mib << 20
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for mode in (0, 1, 2):
+        for blocks in (1024, 2048, 4096, 8192):
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                assert L.rlq_ceiling_read(mode, buf.data_ptr(), n, sink.data_ptr(), blocks, stream.cuda_stream) == 0
+                b.record(stream)
+                torch.cuda.synchronize()
+                best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def measure_ceilings(torch):
+    """Read stream, copy, MFMA rates with the shader clock, LDS rates."""
+    L = ceilings_lib()
+    stream = torch.cuda.current_stream()
+    res = {"hbm_read_gbps": read_peak_gbps(torch), "hbm_copy_gbps": copy_peak_gbps(torch)}
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    blocks, iters = 1024, 2000                      # 4 workgroups of 4 waves per CU
+    waves = blocks * 4
+    clk = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+    names = {0: ("mfma_f32_16x16x32_f16", 2 * 16 * 16 * 32), 1: ("mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32),
+             2: ("mfma_f32_16x16x32_bf8_fp8", 2 * 16 * 16 * 32), 3: ("mfma_f32_16x16x128_f8f6f4 (fp8)",
+                                                                      2 * 16 * 16 * 128),
+             4: ("mfma_f32_32x32x16_f16", 2 * 32 * 32 * 16)}
+    for kind, (name, flop) in names.items():
+        L.rlq_ceiling_mfma(kind, blocks, 10, sink.data_ptr(), clk.data_ptr(), stream.cuda_stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        assert L.rlq_ceiling_mfma(kind, blocks, iters, sink.data_ptr(), clk.data_ptr(), stream.cuda_stream) == 0
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.median(c[:, 0] / c[:, 1]) * 0.1)   # shader cycles per 100 MHz tick
+        cycles = float(np.median(c[:, 0]))
+        res[name] = {"tflops": waves * iters * 8 * flop / t / 1e12,
+                     "cycles_per_mfma_per_simd": cycles / (iters * 8 * 4),  # 4 waves per SIMD
+                     "shader_clock_ghz": ghz}
+    isink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for kind, (name, nbytes) in {0: ("lds_read_b128", 16), 1: ("lds_write_b128", 16),
+                                 2: ("lds_read_b64_tr_b16", 8)}.items():
+        L.rlq_ceiling_lds(kind, 256, 10, isink.data_ptr(), stream.cuda_stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        assert L.rlq_ceiling_lds(kind, 256, 1000, isink.data_ptr(), stream.cuda_stream) == 0
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        res[name + "_gbps_per_cu"] = 1024 * 16 * 1000 * nbytes / t / 1e9
+    return res
+
+
 def timed_loop(torch, stream, fn, n, chunks=1):
     """fn(0) .. fn(n-1) on `stream` with HIP events only at chunk boundaries
     (an event record idles the GPU for a few microseconds, so none goes
@@ -271,10 +363,18 @@ def bench_decode(args, torch, rlq, workloads):
     # over args.steps back-to-back calls, events only every fifth of them.
     log(f"timing {args.steps} decode calls")
     dec_avg, dec_chunks = timed_loop(torch, stream, decode, args.steps, chunks=5)
-    log(f"step {ms_step * 1e3:.1f} us, decode call {dec_avg * 1e3:.1f} us "
-        f"(chunk means {min(dec_chunks) * 1e3:.1f} .. {max(dec_chunks) * 1e3:.1f})")
+    # Distribution: every call bracketed by its own events (at least 50 calls).
+    n_dist = max(50, args.steps)
+    dec_med, dec_p10, dec_p90 = per_call_us(torch, stream, decode, n_dist)
+    # The step loop once more after the decode loops: the two step figures
+    # bracket any drift of the clock over the run.
+    ms_step2, _ = timed_loop(torch, stream, step, args.steps)
+    log(f"step {ms_step * 1e3:.1f} us (again after the decode loops: {ms_step2 * 1e3:.1f} us), decode call "
+        f"{dec_avg * 1e3:.1f} us (chunk means {min(dec_chunks) * 1e3:.1f} .. {max(dec_chunks) * 1e3:.1f}; "
+        f"per call median {dec_med:.1f}, p10 {dec_p10:.1f}, p90 {dec_p90:.1f})")
     copy_gbps = copy_peak_gbps(torch)
-    log(f"device copy rate {copy_gbps:.0f} GB/s")
+    read_gbps = read_peak_gbps(torch)
+    log(f"device copy rate {copy_gbps:.0f} GB/s, read-only stream {read_gbps:.0f} GB/s")
 
     toks = int(ctx.sum())
     alg_bytes = algorithmic_decode_bytes(B, H, ctx, prob.n_sink if prot else 0, prob.n_recent if prot else 0)
@@ -285,7 +385,8 @@ def bench_decode(args, torch, rlq, workloads):
            "kernel": "rlq_mla_decode (many-head kernel + merge kernel)" if H % 64 == 0 else
                      "rlq_mla_decode (split-KV kernel + merge kernel)",
            "algorithmic_bytes_per_launch": alg_bytes, "copy_peak_gbps": copy_gbps,
-           "frac_of_copy_peak": gbps / copy_gbps}
+           "frac_of_copy_peak": gbps / copy_gbps, "read_peak_gbps": read_gbps,
+           "frac_of_read_peak": gbps / read_gbps}
     mfma = {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
             "kernel": "rlq_mla_decode (many-head kernel + merge kernel)" if H % 64 == 0 else
@@ -310,6 +411,8 @@ def bench_decode(args, torch, rlq, workloads):
         "config": {"workload": workload, "batch": B, "context_tokens": toks, "heads": H,
                    "cache_replicas": replicas, "tau": prob.tau, "gain": prob.gain},
         "decode_us": dec_avg * 1e3, "decode_spread": spread(dec_chunks),
+        "decode_call_us": {"median": dec_med, "p10": dec_p10, "p90": dec_p90, "calls": n_dist},
+        "step_us_repeat": ms_step2 * 1e3,
         "decode_hbm_gbps": gbps,
         "roofline": roofline,
     }
@@ -689,7 +792,14 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the GPU's ceilings (HBM read / copy, MFMA, LDS, shader clock)")
     args = ap.parse_args()
+    if args.ceilings:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(measure_ceilings(torch)), flush=True)
+        return
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20

@@ -35,18 +35,29 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librlq)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+# Microbenchmarks of the GPU's ceilings (HBM read stream, MFMA and LDS rates,
+# shader clock) for bench.py's rooflines; not part of the decode path.
+CEILINGS_SOURCES = ("rlq_ceilings.hip",)
+CEILINGS_LIB = os.path.join(PKG, "librlq_ceilings.so")
+
+
+def _compile(srcs, out, verbose, extra_flags=()):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in srcs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    _compile(CEILINGS_SOURCES, CEILINGS_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose, extra_flags)
 
 
 if __name__ == "__main__":

@@ -54,7 +54,7 @@ constexpr uint32_t kPoison = 0x7fbadbadu;
 // end of a tile, is fetched as the tile starts.
 struct CodeLoad {
   u4 cw[2];          // code words [4 q0 + 8h, 4 q0 + 8h + 4) of sub-tile 0 / 1
-  float mu[2], sd[2];
+  float mu, sd;      // (mean, scale) of sub-tile g & 1 (lanes g and g ^ 1 share a table)
 };
 struct RopeLoad {
   u4 rp[2];          // RoPE key elements [16g + 8h, 16g + 8h + 8)
@@ -71,12 +71,9 @@ __device__ inline void load_codes(const DecodeArgs &A, int64_t first, int r16, i
 #pragma unroll
   for (int st = 0; st < 2; ++st)
     L.cw[st] = *(const u4 *)(cw + (uint32_t)((16 * st + r16) * RLQ_WORDS + 4 * q0 + 8 * h));
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const uint32_t m = (16 * st + r16) * 8 + 2 * (g4 >> 1) + h;
-    L.mu[st] = mt[m];
-    L.sd[st] = mt[m + 4];
-  }
+  const uint32_t m = (16 * (g4 & 1) + r16) * 8 + 2 * (g4 >> 1) + h;
+  L.mu = mt[m];
+  L.sd = mt[m + 4];
 }
 __device__ inline void load_rope(const DecodeArgs &A, int64_t first, int r16, int g4, int h,
                                  RopeLoad &L) {
@@ -217,18 +214,21 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
   // The query in fp8 for the score correction of decoded tokens (BF16 sink /
   // recent rows convert to fp16 exactly and need none).
   constexpr bool kCorr = !kProt;
-  u2 q8B[8];
+  i8v q8B[2];  // K-steps 0-3 and 4-7
   if constexpr (kCorr) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) q8B[k] = query_fp8(qB[k]);
+    for (int k = 0; k < 2; ++k)
+      q8B[k] = cat4(query_fp8(qB[4 * k]), query_fp8(qB[4 * k + 1]), query_fp8(qB[4 * k + 2]), query_fp8(qB[4 * k + 3]));
   }
   // Exchange slots of partial scores, [pair][parity][half][sub-tile][64 lanes].
   // A slot holding kPoison in any element is empty: the reader re-poisons a
   // slot after consuming it, so readiness needs no flag and no barrier.
   // The slots are accessed as volatile: a store that publishes a partial and
   // the partner's polling loads are not reordered or merged by the compiler.
-  volatile f4 *xch = (volatile f4 *)(smem + kChatBytes);
-  auto xch_at = [&](int i, int half) -> volatile f4 * { return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64; };
+  volatile lds_f4 *xch = (volatile lds_f4 *)(smem + kChatBytes);
+  auto xch_at = [&](int i, int half) -> volatile lds_f4 * {
+    return xch + (((pr * 2 + (i & 1)) * 2 + half) * 2) * 64;
+  };
   bool xch_lost = false;  // a poll gave up (wave-uniform)
   const f4 poison = __builtin_bit_cast(f4, u4{kPoison, kPoison, kPoison, kPoison});
 #pragma unroll
@@ -355,29 +355,42 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     constexpr bool kScore = decltype(score_c)::value;
     constexpr bool kValue = decltype(value_c)::value;
     f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-    // The correction accumulates apart (fp8 MFMAs only) and joins with a
-    // VALU add at the end of the tile.
-    f4 accR[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    // Residual operands of the last four K-steps; every second pair of
+    // K-steps ends with their correction, chained on the score accumulator.
+    i8v res[2];
+    auto score_one = [&](int kl, int st) {
+      const Dec8 v = dec(kl, st);
+      *(u4 *)(wl + st * kSubBytes + kl * 1024 + 16 * chat_slot(kl, g4, r16)) = v.v;
+      acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v.v), qB[kl], acc[st], 0, 0, 0);
+      res[st][2 * (kl & 3)] = (int)v.r[0];
+      res[st][2 * (kl & 3) + 1] = (int)v.r[1];
+    };
     auto score_pair = [&](int p) {
+      if (!kCorr || !(p & 1)) {
 #pragma unroll
-      for (int kl = 2 * p; kl < 2 * p + 2; ++kl)
+        for (int kl = 2 * p; kl < 2 * p + 2; ++kl)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) score_one(kl, st);
+      } else {
+        // Sub-tile by sub-tile, so sub-tile 0's residuals are consumed (and
+        // their registers freed) before sub-tile 1's are made.
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const Dec8 v = dec(kl, st);
-          *(u4 *)(wl + st * kSubBytes + kl * 1024 + 16 * chat_slot(kl, g4, r16)) = v.v;
-          acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, v.v), qB[kl], acc[st], 0, 0, 0);
-          if constexpr (kCorr) accR[st] = correct_scores(v.r, q8B[kl], accR[st]);
+#pragma unroll
+          for (int kl = 2 * p; kl < 2 * p + 2; ++kl) score_one(kl, st);
+          acc[st] = correct_scores4(res[st], q8B[p >> 1], acc[st]);
         }
+      }
     };
     half8 av0[4];
     f4 o0, o1;
-    volatile f4 *other = xch_at(i - 1, h ^ 1);
+    volatile lds_f4 *other = xch_at(i - 1, h ^ 1);
     if constexpr (kValue) {
       // This wave's partial of tile i-1, finished in the previous step, is
       // published now rather than at the end of that step, so no wave waits
       // there for its last MFMAs.  The partner does the same; its partial is
       // read here and consumed after part 1.
-      volatile f4 *mine = xch_at(i - 1, h);
+      volatile lds_f4 *mine = xch_at(i - 1, h);
       mine[lane] = acc_prev[0];
       mine[64 + lane] = acc_prev[1];
       o0 = other[lane];
@@ -414,13 +427,14 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
       if constexpr (kValue) value_pair(p, av);
     }
     if constexpr (kScore) {
-      mfma_type_switch();  // f16 -> bf16 on acc
+      mfma_type_switch();  // the accumulator comes from an f8f6f4 product (bf16 then reads it safely; the
+                           // fence keeps a gap should an f16 product ever precede it)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
       tail();
-      acc_prev[0] = kCorr ? acc[0] + accR[0] : acc[0];
-      acc_prev[1] = kCorr ? acc[1] + accR[1] : acc[1];
+      acc_prev[0] = acc[0];
+      acc_prev[1] = acc[1];
     }
   };
   auto no_dec = [](int, int) -> Dec8 { return Dec8{u4{0, 0, 0, 0}, u2{0, 0}}; };
@@ -432,13 +446,18 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &A, c
     auto c0_of = [&](int i) { return t_begin + kWaveTok * (tile0 + i); };
     // Decode tables of the tile being decoded; the tail of each step replaces
     // them with the next tile's.
+    // Lanes g and g ^ 1 (lane groups 0/1, 2/3) decode the same token and
+    // group: the even lane group builds sub-tile 0's table, the odd one
+    // sub-tile 1's, and a permlane16 swap hands each its partner's.
     Lut lut[2];
     auto build_lut = [&](const CodeLoad &L, int i) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int t = c0_of(i) + 16 * st + r16;
-        lut[st] = make_lut(L.mu[st], L.sd[st], A.gain, A.level_inner, A.level_outer, t >= vlo && t < vhi);
-      }
+      const int t = c0_of(i) + 16 * (g4 & 1) + r16;
+      const Lut mine = make_lut(L.mu, L.sd, A.gain, A.level_inner, A.level_outer, t >= vlo && t < vhi);
+      auto lo = __builtin_amdgcn_permlane16_swap(mine.lo, mine.lo, false, false);
+      auto hi = __builtin_amdgcn_permlane16_swap(mine.hi, mine.hi, false, false);
+      auto rs = __builtin_amdgcn_permlane16_swap(mine.rs, mine.rs, false, false);
+      lut[0] = Lut{lo[0], hi[0], rs[0]};
+      lut[1] = Lut{lo[1], hi[1], rs[1]};
     };
     RopeLoad rb;
     // Step i: `cur` holds tile i's codes, `next` tile i+1's, `far` takes

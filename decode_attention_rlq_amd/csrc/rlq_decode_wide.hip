@@ -272,9 +272,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
   for (int k = 0; k < 8; ++k) qB[k] = *(const half8 *)(smem + qslot(16 * pr + r16, 8 * h + k, g4));
   __syncthreads();  // query staging done: the buffers below may be overwritten
   // The query in fp8 for the score correction.
-  u2 q8B[8];
+  i8v q8B[2];  // K-steps 0-3 and 4-7
 #pragma unroll
-  for (int k = 0; k < 8; ++k) q8B[k] = query_fp8(qB[k]);
+  for (int k = 0; k < 2; ++k)
+    q8B[k] = cat4(query_fp8(qB[4 * k]), query_fp8(qB[4 * k + 1]), query_fp8(qB[4 * k + 2]), query_fp8(qB[4 * k + 3]));
 
   // ---- fill role of this lane: sub-tile fst, 128-coordinate group fgrp,
   // token row fr, code words W0, W0 + 1 (coordinates 16 W0 .. 16 W0 + 31).
@@ -482,11 +483,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
         const u4 wv = *(const u4 *)(cb + (16 * st + r16) * kCodeRow + 4 * (4 * wq0 + 8 * h));
         const uint32_t rt = *(const uint32_t *)(cb + kCodeTabOff + 4 * (4 * (16 * st + r16) + 2 * (g4 >> 1) + h));
 #pragma unroll
-        for (int kl = 0; kl < 8; ++kl) acc[st] = correct_scores(resid8(wv[kl >> 1], kl & 1, rt), q8B[kl], acc[st]);
+        for (int k4 = 0; k4 < 2; ++k4)
+          acc[st] = correct_scores4(cat4(resid8(wv[2 * k4], 0, rt), resid8(wv[2 * k4], 1, rt),
+                                         resid8(wv[2 * k4 + 1], 0, rt), resid8(wv[2 * k4 + 1], 1, rt)),
+                                    q8B[k4], acc[st]);
       }
     };
     Lut fl;
-    if constexpr (kScore) fl = fill_lut(i + 1, F);
+    if constexpr (kScore) {
+      fl = fill_lut(i + 1, F);
+      // The tile's scores start with the RoPE part (bf16, from LDS), then the
+      // f16 content products and the f8f6f4 corrections chain on it (an f16
+      // product may take its accumulator from a bf16 one, and an f8f6f4 one
+      // from an f16 one; not the other way round from f16 to bf16).
+      const unsigned char *rb = rbuf(k);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u4 rp = *(const u4 *)(rb + rope_off(16 * st + r16, 2 * g4 + h));
+        acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp), qrB, acc[st], 0, 0, 0);
+      }
+    }
     half8 av0[4];
     if constexpr (kValue) {
       // Both partials of tile i-1 come back from the exchange slots (the own
@@ -510,16 +526,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_wide_kernel(DecodeAr
       if constexpr (kValue) value_pair(p, av);
     }
     if constexpr (kScore) {
-      const unsigned char *rb = rbuf(k);
-      u4 rp[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) rp[st] = *(const u4 *)(rb + rope_off(16 * st + r16, 2 * g4 + h));
-      mfma_type_switch();  // f16 -> bf8 x fp8 on acc
       correct();
-      mfma_type_switch();  // bf8 x fp8 -> bf16 on acc
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rp[st]), qrB, acc[st], 0, 0, 0);
       fill_part(kn, F, fl, 3);
       fill_end(i + 1, kn, F, fl);
       f4 *mine = xch_at(i, h);
