@@ -352,10 +352,7 @@ static int decode_call(const rlq_layer_params *p, const rlq_cache *cache,
   a.spin_limit = a.force_xch_timeout ? 2 : (1 << 16);
   if (wide) {
     // Many heads: balanced work items, each 32-token tile decoded once per 64 heads.
-    const size_t parts = (size_t)wplan.item_slots * (heads / 16);
-    a.part_o = (float *)workspace;
-    a.part_ml = a.part_o + parts * rlq::kPartialFloats;
-    a.plan = (int32_t *)(a.part_ml + parts * 32);
+    rlq::wide_workspace_layout(a, workspace, batch, heads, wplan);
     return hip_status(rlq::launch_decode_wide(a, batch, (hipStream_t)stream));
   }
   const size_t parts = (size_t)batch * (heads / 16) * (plan.splits + a.prot);
@@ -472,10 +469,7 @@ int rlq_mla_extend(const rlq_layer_params *p, const rlq_cache *cache,
   a.q_heads = heads;
   a.force_xch_timeout = 0;
   a.spin_limit = 1 << 16;
-  const size_t parts = (size_t)wplan.item_slots * (size_t)(rows / 16);
-  a.part_o = (float *)workspace;
-  a.part_ml = a.part_o + parts * rlq::kPartialFloats;
-  a.plan = (int32_t *)(a.part_ml + parts * 32);
+  rlq::wide_workspace_layout(a, workspace, batch, (int32_t)rows, wplan);
   return hip_status(rlq::launch_decode_wide(a, batch, (hipStream_t)stream));
 }
 

@@ -140,7 +140,7 @@ hipError_t launch_decode(const DecodeArgs &a, int32_t batch, hipStream_t stream)
 constexpr int kWideHeads = 64;
 constexpr int kResidentWide = 256;
 constexpr int kMinItemTiles = 16;
-constexpr int kMaxItemPages = 1024;
+constexpr int kMaxItemPages = 768;
 constexpr int kMaxItemTiles = 2 * (kMaxItemPages - 1);
 
 inline bool use_wide(int32_t heads) { return heads % kWideHeads == 0; }
@@ -148,9 +148,13 @@ inline bool use_wide(int32_t heads) { return heads % kWideHeads == 0; }
 struct WidePlan {
   int32_t item_slots;
   int32_t item_target;
+  int32_t partials;  // 1 if a request can span several items (partials + merge)
 };
 WidePlan plan_wide(int32_t batch, int32_t heads, int32_t max_ctx_len);
 size_t wide_workspace_bytes(int32_t batch, int32_t heads, const WidePlan &plan);
+// Points a.plan / a.part_o / a.part_ml into a workspace of
+// wide_workspace_bytes (part_o and part_ml null without partials).
+void wide_workspace_layout(DecodeArgs &a, void *workspace, int32_t batch, int32_t heads, const WidePlan &plan);
 hipError_t launch_decode_wide(const DecodeArgs &a, int32_t batch, hipStream_t stream);
 
 // Extend: the many-head kernel over (query, head) rows.  Padded row count of

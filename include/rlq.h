@@ -227,7 +227,10 @@ int rlq_quantize_append(const rlq_layer_params *p, const rlq_cache *cache,
  * Workspace (bytes) that rlq_mla_decode needs for this batch, head count and
  * maximum context length: split-KV partials (unnormalised output, running max
  * and sum per split and head) and, when heads is a multiple of 64, a table of
- * each request's work items (two int32 per request).  Errors: RLQ_EINVAL (also
+ * each request's work items (two int32 per request) followed by partials per
+ * work-item slot and 32 heads (64 KB + 256 bytes), which are left out when
+ * every request is one work item (batch * heads / 64 >= 512 and max_ctx_len
+ * <= 49,088: the requests' rows are then written directly).  Errors: RLQ_EINVAL (also
  * for max_ctx_len above RLQ_MAX_CTX, and for batch * heads / 16 above 65535
  * when heads is not a multiple of 64).
  */
@@ -288,7 +291,7 @@ int rlq_mla_decode(const rlq_layer_params *p, const rlq_cache *cache,
  * array and race; serialize them.  The array needs no initialisation.
  * Errors: as rlq_mla_decode; RLQ_ENOSPC when rlq_mla_decode_workspace_size()
  * for these arguments exceeds RLQ_NOALLOC_SCRATCH_BYTES (e.g. batch 2 at
- * RLQ_MAX_CTX with 128 heads needs 34 MB, which fits).
+ * RLQ_MAX_CTX with 128 heads needs 46 MB, which fits).
  */
 int rlq_mla_decode_noalloc(const rlq_layer_params *p, const rlq_cache *cache,
                            const uint16_t *q_c_bf16, const uint16_t *q_r_bf16,
@@ -298,12 +301,16 @@ int rlq_mla_decode_noalloc(const rlq_layer_params *p, const rlq_cache *cache,
                            float *out, float *lse, void *stream);
 
 /*
- * Workspace (bytes) that rlq_mla_extend needs: split partials for
- * (query, head) rows, max_q_len * heads rows rounded up to 64 per request,
- * and the work-item table.  Errors: RLQ_EINVAL (heads, batch, max_q_len < 1,
- * max_ctx_len above RLQ_MAX_CTX, or a row count beyond the launch limits:
- * rows / 64 at most 65535 and batch * rows / 16 at most 2^30).  The partials
- * take 32.9 KB per 16 rows and work item: chunk long prompts.
+ * Workspace (bytes) that rlq_mla_extend needs: the work-item table (two int32
+ * per request, padded to 256 bytes) and, when a request can span several work
+ * items, split partials for (query, head) rows, max_q_len * heads rows
+ * rounded up to 64 per request.  With batch * rows / 64 >= 512 and
+ * max_ctx_len <= 49,088 every request is one work item and writes its rows
+ * directly: the table alone (e.g. 4 requests of 8192 queries).  Otherwise the
+ * partials take 64 KB + 256 bytes per 32 rows and work-item slot.  Errors:
+ * RLQ_EINVAL (heads, batch, max_q_len < 1, max_ctx_len above RLQ_MAX_CTX, or
+ * a row count beyond the launch limits: rows / 64 at most 65535 and
+ * batch * rows / 16 at most 2^30).
  */
 int rlq_mla_extend_workspace_size(int32_t batch, int32_t heads, int32_t max_q_len,
                                   int32_t max_ctx_len, size_t *bytes);

@@ -97,22 +97,31 @@ def test_workspace_splits_cover_the_context(lib, batch, heads, ctx):
 
 
 @pytest.mark.parametrize("batch,heads,ctx", [(32, 128, 59297), (4, 64, 262144), (1, 128, 1 << 22),
-                                              (200, 128, 1000), (3, 128, 0), (300, 64, 70000)])
+                                              (200, 128, 1000), (3, 128, 0), (300, 64, 70000),
+                                              (512, 64, 1000), (256, 128, 70000)])
 def test_workspace_many_heads_holds_every_item(lib, batch, heads, ctx):
-    """With a multiple of 64 heads the workspace holds, per work-item slot and
-    16-head tile, a 16 x 512 fp32 partial + 32 floats, then two ints per
-    request.  The slots cover one round of workgroups (256 per 64 heads),
-    and at least ceil(tiles / 2046) items per request (an item spans at most
-    2046 tiles of 32 tokens), in a multiple of 8."""
-    per = (16 * 512 + 32) * 4
+    """With a multiple of 64 heads the workspace holds the plan (two ints per
+    request, padded to 256 bytes), then, when a request can span several
+    work items, per item slot and 32-row tile a 32 x 512 fp32 partial + 64
+    floats.  An item spans at most 1534 tiles of 32 tokens.  With fewer than
+    512 (request, 64-row group) workgroups the slots cover one round of
+    workgroups (256 per 64 heads) in a multiple of 8; with more, every request
+    is one item unless its context needs more, and without such a request
+    there are no partials."""
+    per = (32 * 512 + 64) * 4
+    plan = -(-8 * batch // 256) * 256
     size = rlq.decode_workspace_size(batch, heads, ctx)
-    parts, rem = divmod(size - 8 * batch, per)
-    assert rem == 0 and parts % (heads // 16) == 0
-    slots = parts // (heads // 16)
+    parts, rem = divmod(size - plan, per)
+    assert rem == 0 and parts % (heads // 32) == 0
+    slots = parts // (heads // 32)
     tiles = -(-ctx // 32)
-    assert slots % 8 == 0
-    assert slots >= 256 // (heads // 64)
-    assert slots >= batch * max(1, -(-tiles // 2046))
+    per_req = max(1, -(-tiles // 1534))
+    if batch * (heads // 64) >= 512:
+        assert slots == (batch * per_req if per_req > 1 else 0)
+    else:
+        assert slots % 8 == 0
+        assert slots >= 256 // (heads // 64)
+        assert slots >= batch * per_req
 
 
 def test_validation_rejects_before_any_launch(lib):
@@ -150,12 +159,16 @@ def test_validation_rejects_before_any_launch(lib):
 def test_extend_workspace_and_validation(lib):
     """rlq_mla_extend: (query, head) rows per request padded to 64, partials
     per item slot and 16-row tile; validation fails before any launch."""
-    per = (16 * 512 + 32) * 4
-    for batch, heads, max_q, ctx in [(4, 16, 512, 33280), (2, 128, 7, 1000), (3, 16, 1, 64)]:
+    per = (32 * 512 + 64) * 4
+    for batch, heads, max_q, ctx in [(2, 128, 7, 1000), (3, 16, 1, 64), (1, 16, 64, 40000)]:
         size = rlq.extend_workspace_size(batch, heads, max_q, ctx)
         rows = -(-max_q * heads // 64) * 64
-        parts, rem = divmod(size - 8 * batch, per)
-        assert rem == 0 and parts % (rows // 16) == 0 and (parts // (rows // 16)) % 8 == 0
+        parts, rem = divmod(size - 256, per)
+        assert rem == 0 and parts % (rows // 32) == 0 and (parts // (rows // 32)) % 8 == 0
+    # Many (request, 64-row group) workgroups: one item per request, no
+    # partials, only the plan (4 x 8192 queries of 16 or 128 heads).
+    for batch, heads, max_q, ctx in [(4, 16, 512, 33280), (4, 16, 8192, 32768), (4, 128, 8192, 40000)]:
+        assert rlq.extend_workspace_size(batch, heads, max_q, ctx) == 256
     for bad in [(1, 24, 4, 100), (0, 16, 4, 100), (1, 16, 0, 100), (1, 16, 101, 100), (1, 144, 4, 100),
                 (1, 128, 40000, 40000)]:  # the last exceeds the launch grid (rows / 64 > 65535)
         with pytest.raises(ValueError):
