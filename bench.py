@@ -32,6 +32,14 @@ for 128 heads); `cpu_baseline` times the CPU oracle on a bounded sample of the
 same work.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+Tools beside the benchmark (each prints one JSON line and exits):
+  --ceilings               measured ceilings of this GPU: read-only HBM stream and
+                           device copy, MFMA rates of the instruction shapes the
+                           kernels use (one wave per SIMD, with the shader clock),
+                           LDS read / write / transposed-read rates per CU
+  --copy-calibration MIB   a plain device copy, the reference for the
+                           FETCH_SIZE / WRITE_SIZE counter scale
 """
 
 from __future__ import annotations
@@ -197,7 +205,8 @@ def measure_ceilings(torch):
     names = {0: ("mfma_f32_16x16x32_f16", 2 * 16 * 16 * 32), 1: ("mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32),
              2: ("mfma_f32_16x16x32_bf8_fp8", 2 * 16 * 16 * 32), 3: ("mfma_f32_16x16x128_f8f6f4 (fp8)",
                                                                       2 * 16 * 16 * 128),
-             4: ("mfma_f32_32x32x16_f16", 2 * 32 * 32 * 16)}
+             4: ("mfma_f32_32x32x16_f16", 2 * 32 * 32 * 16),
+             5: ("mfma_f32_32x32x16_f16 + 8 independent v_fma_f32 per MFMA", 2 * 32 * 32 * 16)}
     for kind, (name, flop) in names.items():
         L.rlq_ceiling_mfma(kind, blocks, 10, sink.data_ptr(), clk.data_ptr(), stream.cuda_stream)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -208,10 +217,18 @@ def measure_ceilings(torch):
         t = a.elapsed_time(b) * 1e-3
         c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
         ghz = float(np.median(c[:, 0] / c[:, 1]) * 0.1)   # shader cycles per 100 MHz tick
-        cycles = float(np.median(c[:, 0]))
-        res[name] = {"tflops": waves * iters * 8 * flop / t / 1e12,
-                     "cycles_per_mfma_per_simd": cycles / (iters * 8 * 4),  # 4 waves per SIMD
-                     "shader_clock_ghz": ghz}
+        # One workgroup of 4 waves per CU (256 workgroups): one wave per
+        # SIMD, so a wave's own clock gives the SIMD's cycles per MFMA with
+        # eight independent accumulators, and the rate follows from the clock.
+        assert L.rlq_ceiling_mfma(kind, 256, iters, sink.data_ptr(), clk.data_ptr(), stream.cuda_stream) == 0
+        torch.cuda.synchronize()
+        c1 = clk.view(-1, 2)[:1024].cpu().numpy().astype(np.float64)
+        cyc1 = float(np.median(c1[:, 0])) / (iters * 8)
+        ghz1 = float(np.median(c1[:, 0] / c1[:, 1]) * 0.1)
+        res[name] = {"tflops_event_timed": waves * iters * 8 * flop / t / 1e12,
+                     "cycles_per_mfma_one_wave_per_simd": cyc1,
+                     "tflops_at_that_rate": flop * 1024 * ghz1 * 1e9 / cyc1 / 1e12,
+                     "shader_clock_ghz": ghz1}
     isink = torch.zeros(4, dtype=torch.int32, device="cuda")
     for kind, (name, nbytes) in {0: ("lds_read_b128", 16), 1: ("lds_write_b128", 16),
                                  2: ("lds_read_b64_tr_b16", 8)}.items():

@@ -40,7 +40,9 @@ __global__ __launch_bounds__(256) void read_kernel(const u4 *__restrict__ src, i
 }
 
 // kind 0: v_mfma_f32_16x16x32_f16, 1: _bf16, 2: _bf8_fp8 (16x16x32), 3:
-// v_mfma_f32_16x16x128_f8f6f4 with fp8 operands, 4: v_mfma_f32_32x32x16_f16.  Eight independent
+// v_mfma_f32_16x16x128_f8f6f4 with fp8 operands, 4: v_mfma_f32_32x32x16_f16,
+// 5: kind 4 with eight independent fp32 FMAs issued after each MFMA (how much
+// VALU work one wave can issue under its own MFMAs).  Eight independent
 // accumulators per wave, `iters` rounds.  Lane 0 of each wave records the
 // shader-clock counter (s_memtime) and the 100 MHz reference counter
 // (s_memrealtime) around the loop.
@@ -51,11 +53,15 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float *sink, int64
   a4 &= u4{0x3b3b3b3bu, 0x3b3b3b3bu, 0x3b3b3b3bu, 0x3b3b3b3bu};  // small finite fp16 / bf16 / fp8 values
   typedef float f16v __attribute__((ext_vector_type(16)));
   f4 acc[8];
-  f16v acc16[kKind == 4 ? 8 : 1];
+  constexpr bool k32 = kKind == 4 || kKind == 5;
+  f16v acc16[k32 ? 8 : 1];
+  float fv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fv[j] = (float)(threadIdx.x + j);
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < (kKind == 4 ? 8 : 1); ++j) acc16[j] = f16v{};
+  for (int j = 0; j < (k32 ? 8 : 1); ++j) acc16[j] = f16v{};
   const int64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -76,6 +82,10 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float *sink, int64
         // 32x32x16 f16: four 16x16 accumulators' worth of output per product
         const half8 a = __builtin_bit_cast(half8, a4);
         acc16[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, acc16[j], 0, 0, 0);
+        if constexpr (kKind == 5) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) fv[x] = __builtin_fmaf(fv[x], 1.0001f, 0.5f);
+        }
       }
     }
   }
@@ -83,9 +93,13 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float *sink, int64
   f4 s = acc[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) s += acc[j];
-  if constexpr (kKind == 4) {
+  if constexpr (k32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[0] += acc16[j][0] + acc16[j][15];
+  }
+  if constexpr (kKind == 5) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[1] += fv[j];
   }
   if (s[0] == 1234.5f) sink[0] = s[1];
   if ((threadIdx.x & 63) == 0) {
@@ -156,6 +170,7 @@ int rlq_ceiling_mfma(int32_t kind, int32_t blocks, int32_t iters, float *sink, i
     case 2: hipLaunchKernelGGL(mfma_kernel<2>, dim3(blocks), dim3(256), 0, s, iters, sink, clk); break;
     case 3: hipLaunchKernelGGL(mfma_kernel<3>, dim3(blocks), dim3(256), 0, s, iters, sink, clk); break;
     case 4: hipLaunchKernelGGL(mfma_kernel<4>, dim3(blocks), dim3(256), 0, s, iters, sink, clk); break;
+    case 5: hipLaunchKernelGGL(mfma_kernel<5>, dim3(blocks), dim3(256), 0, s, iters, sink, clk); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
