@@ -231,10 +231,12 @@ __global__ __launch_bounds__(64 * kBulkWaves, 1) void append_kernel(AppendArgs a
   // operand reads of 16 consecutive rows over distinct banks.
   auto chunk = [](int k, int r, int c) { return k * kRSlice + 64 * r + 16 * (c ^ ((r >> 2) & 3)); };
   if (a.latent_rot == nullptr) {
+    // Consecutive lanes fill consecutive chunks of one K-slice (a wave writes
+    // one contiguous 1 KB block, free of bank conflicts).
     for (int i = threadIdx.x; i < RLQ_GROUP * RLQ_DC / 8; i += 64 * kBulkWaves) {
-      const int r = i >> 6, kc = i & 63;  // row, 8-element chunk along K
-      *(u4 *)(rs + chunk(kc >> 2, r, kc & 3)) =
-          *(const u4 *)(a.rotation + (size_t)(G * RLQ_GROUP + r) * RLQ_DC + 8 * kc);
+      const int c = i & 3, r = (i >> 2) & (RLQ_GROUP - 1), k = i >> 9;  // chunk, row, K-slice
+      *(u4 *)(rs + chunk(k, r, c)) =
+          *(const u4 *)(a.rotation + (size_t)(G * RLQ_GROUP + r) * RLQ_DC + 8 * (4 * k + c));
     }
   }
   // The request table, so that finding a token's request and position needs

@@ -531,6 +531,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void decode_wide_kernel(DecodeArgs
   // Past the item's end the fill repeats its last tile into a free slot, so
   // every scoring iteration issues the same loads.  kScore / kValue switch off
   // the first and last halves.
+  // Operands of the first value group of the next iteration (tile i's M-tiles
+  // 0 and 1), read in iteration i's tail before the barrier: tile i's ĉ is
+  // complete since the barrier that opened iteration i.
+  half8 vnext[2][2];
   auto iteration = [&](auto score_c, auto value_c, int i, int k, FillLoad &F) {
     constexpr bool kScore = decltype(score_c)::value;
     constexpr bool kValue = decltype(value_c)::value;
@@ -588,6 +592,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void decode_wide_kernel(DecodeArgs
         o4[q] = oth[64 * q];
         m4[q] = own[64 * q];
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vop[0][u][ks] = vnext[u][ks];
     }
     if constexpr (kScore) {
       fl = fill_lut(i + 1, F);
@@ -607,12 +615,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void decode_wide_kernel(DecodeArgs
         const i8v r = cat4(resid8(w0, 0, rt), resid8(w0, 1, rt), resid8(w1, 0, rt), resid8(w1, 1, rt));
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r, q8B[j], acc, 1, 0, 0, 0, 0, 0);
       }
-      if constexpr (kValue) load_v(0, 0);
       load_s(1, 1);
       mfma_type_gap(acc);
       mfma_s(0, 0);
-    } else if constexpr (kValue) {
-      load_v(0, 0);
     }
     if constexpr (kValue) softmax(m4, o4, kWaveTok * (it.tb + i - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -640,6 +645,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void decode_wide_kernel(DecodeArgs
       for (int q = 0; q < 4; ++q) mine[64 * q] = f4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
       __builtin_amdgcn_sched_barrier(0);
       load_fill(i + 4, F);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vnext[u][ks] = tr_load(cs, u, ks);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     }
